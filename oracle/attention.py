@@ -1,0 +1,213 @@
+"""Plain fp64 CPU oracle for exact attention, its streamed form and the split-KV merge.
+
+TEST INFRASTRUCTURE ONLY. This module is the yardstick the GPU library is
+checked against. Only the tests, the smoke check and the benchmark's CPU
+baseline may import it; the library itself never calls it and has no CPU
+fallback.
+
+Sources (three web pages on IO-aware attention):
+  [IOP]   "I/O-Aware Kernels", IOP Systems blog, sections "The Memory Bottleneck"
+          and "FlashAttention".
+  [GRASP] "Tracing Tiled QKV Data Movement in FlashAttention's Memory
+          Hierarchy", grasp.study lesson, sections 2 and 3.
+  [ILP]   "FlashAttention & IO-aware attention", inference-learning-path
+          interview page, sections "Direct answer", "Deep dive", "Code",
+          "Interviewer follow-ups".
+
+What is computed. [IOP, The Memory Bottleneck] and [ILP, Direct answer] define
+attention as scores Q K^T, a row softmax, and a product with V; [ILP, Direct
+answer] states that the streamed (online-softmax) form yields exactly that
+function. So the oracle is the definition itself, evaluated in float64 on the
+bf16 input values widened exactly:
+
+    s_ij   = scale * sum_c Q[i,c] K[j,c]          for j in A(i)
+    M_i    = max_{j in A(i)} s_ij
+    w_ij   = exp(s_ij - M_i),  L_i = sum_j w_ij
+    O[i,:] = sum_j w_ij V[j,:] / L_i
+    LSE_i  = M_i + ln L_i                          (natural log)
+
+Readings where the pages are silent (each one is listed in the design notes):
+  * A(i) is every key when not causal; when causal it is {j : j <= i + Skv - Sq}
+    (bottom-right alignment, equal to j <= i when Sq == Skv).
+  * A row with no visible key has O = 0 and LSE = -inf.
+  * Grouped-query heads: query head h reads KV head floor(h * Hkv / Hq).
+  * ``scale`` is used as the float32 value the library receives, widened.
+  * Subtracting M_i leaves the result unchanged mathematically; it keeps
+    exp() finite ([ILP, Interviewer follow-ups] on why the running max exists).
+
+Score rows are formed one block of query rows at a time; nothing else is
+blocked, fused or reordered.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def widen_bf16(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float64, exactly (bf16 is the top half of fp32)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def _sigma(scale: float) -> float:
+    return float(np.float32(scale))
+
+
+def kv_head_of(h: int, Hq: int, Hkv: int) -> int:
+    """KV head read by query head h: contiguous groups of Hq / Hkv query heads."""
+    return (h * Hkv) // Hq
+
+
+def visible_keys(i: int, Sq: int, Skv: int, causal: bool) -> int:
+    """Number of keys query row i may attend to; keys are 0 .. n-1."""
+    if not causal:
+        return Skv
+    return max(0, min(Skv, i + Skv - Sq + 1))
+
+
+def attention_rows(q_rows: np.ndarray, K: np.ndarray, V: np.ndarray, rows: np.ndarray,
+                   Sq: int, causal: bool, scale: float):
+    """Exact attention for selected query rows of one (batch, head).
+
+    q_rows [n, d] f64 are the query vectors of rows ``rows`` (indices into the
+    Sq query positions); K, V [Skv, d] f64 are that head's keys and values.
+    Returns O [n, d] and LSE [n] in float64.
+    """
+    rows = np.asarray(rows)
+    Skv = K.shape[0]
+    sigma = _sigma(scale)
+    s = sigma * (q_rows @ K.T)                                   # [n, Skv]
+    nvis = np.array([visible_keys(int(i), Sq, Skv, causal) for i in rows])
+    keep = np.arange(Skv)[None, :] < nvis[:, None]
+    s = np.where(keep, s, -np.inf)
+    O = np.zeros((len(rows), V.shape[1]))
+    LSE = np.full(len(rows), -np.inf)
+    live = nvis > 0
+    if live.any():
+        sl = s[live]
+        M = sl.max(axis=1)
+        w = np.exp(sl - M[:, None])                              # masked -> exp(-inf) = 0
+        L = w.sum(axis=1)
+        O[live] = (w @ V) / L[:, None]
+        LSE[live] = M + np.log(L)
+    return O, LSE
+
+
+def attention_ref(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, causal: bool,
+                  scale: float, row_block: int = 512):
+    """Exact attention over whole tensors.
+
+    q [B,Sq,Hq,d], k and v [B,Skv,Hkv,d], all float64.
+    Returns O [B,Sq,Hq,d] and LSE [B,Hq,Sq], float64.
+    """
+    B, Sq, Hq, d = q.shape
+    Bk, Skv, Hkv, dk = k.shape
+    if Bk != B or dk != d or v.shape != k.shape or Hq % Hkv != 0:
+        raise ValueError("inconsistent shapes")
+    O = np.zeros((B, Sq, Hq, d))
+    LSE = np.full((B, Hq, Sq), -np.inf)
+    for b in range(B):
+        for h in range(Hq):
+            hk = kv_head_of(h, Hq, Hkv)
+            K, V = k[b, :, hk, :], v[b, :, hk, :]
+            for r0 in range(0, Sq, row_block):
+                rows = np.arange(r0, min(Sq, r0 + row_block))
+                o, l = attention_rows(q[b, rows, h, :], K, V, rows, Sq, causal, scale)
+                O[b, rows, h, :] = o
+                LSE[b, h, rows] = l
+    return O, LSE
+
+
+def decode_ref(q: np.ndarray, kc: np.ndarray, vc: np.ndarray, *, scale: float):
+    """Single-query decode: q [B,Hq,d], caches [B,Skv,Hkv,d] -> O [B,Hq,d], LSE [B,Hq].
+
+    [ILP, Direct answer]: a decode step has one query, so its scores are a
+    1 x Skv vector over every cached key (no mask).
+    """
+    O, LSE = attention_ref(q[:, None], kc, vc, causal=False, scale=scale)
+    return O[:, 0], LSE[:, :, 0]
+
+
+def online_ref(q: np.ndarray, K: np.ndarray, V: np.ndarray, *, scale: float,
+               block: int = 2, per_element: bool = True):
+    """Streamed softmax for one query row, in the pages' running-statistics form.
+
+    [ILP, Direct answer] and [IOP, FlashAttention]: walk the keys left to right
+    in blocks while keeping a running max m, a normaliser l and an output
+    accumulator acc. When a block raises the max, scale l and acc by
+    exp(m - m_new) before adding the block's terms; divide by l once at the end.
+    ``per_element`` updates the statistics after every key inside a block (as
+    the page's CPU example does); otherwise once per block.
+    Returns (o [d], lse) in float64.
+    """
+    sigma = _sigma(scale)
+    m, l = -math.inf, 0.0
+    acc = np.zeros(V.shape[1])
+    for j0 in range(0, K.shape[0], block):
+        Kb, Vb = K[j0:j0 + block], V[j0:j0 + block]
+        if per_element:
+            for kj, vj in zip(Kb, Vb):
+                s = sigma * float(np.dot(q, kj))
+                m_new = max(m, s)
+                c = math.exp(m - m_new) if m != -math.inf else 0.0
+                p = math.exp(s - m_new)
+                l = l * c + p
+                acc = acc * c + p * vj
+                m = m_new
+        else:
+            s = sigma * (Kb @ q)
+            m_new = max(m, float(s.max()))
+            c = math.exp(m - m_new) if m != -math.inf else 0.0
+            p = np.exp(s - m_new)
+            l = l * c + float(p.sum())
+            acc = acc * c + p @ Vb
+            m = m_new
+    if l == 0.0:
+        return np.zeros(V.shape[1]), -math.inf
+    return acc / l, m + math.log(l)
+
+
+def split_partials_ref(q: np.ndarray, kc: np.ndarray, vc: np.ndarray, *, scale: float,
+                       bounds: list):
+    """Per-chunk decode partials, each chunk normalised on its own.
+
+    [ILP, Deep dive] names splitting the KV length across compute units for
+    decode. Chunk c covers keys bounds[c] .. bounds[c+1]-1 and yields the
+    attention of the query over those keys alone: O_c and lambda_c (its LSE).
+    An empty chunk gives O_c = 0 and lambda_c = -inf.
+    Returns part_o [B,Hq,n,d] and part_lse [B,Hq,n].
+    """
+    B, Hq, d = q.shape
+    n = len(bounds) - 1
+    part_o = np.zeros((B, Hq, n, d))
+    part_lse = np.full((B, Hq, n), -np.inf)
+    for c in range(n):
+        lo, hi = bounds[c], bounds[c + 1]
+        if hi > lo:
+            o, l = decode_ref(q, kc[:, lo:hi], vc[:, lo:hi], scale=scale)
+            part_o[:, :, c] = o
+            part_lse[:, :, c] = l
+    return part_o, part_lse
+
+
+def combine_ref(part_o: np.ndarray, part_lse: np.ndarray):
+    """Merge chunk partials by log-sum-exp.
+
+    The chunk-level form of the running-max rescale ([ILP, Direct answer]):
+    chunk c stands for exp(lambda_c) total weight with normalised output O_c, so
+        Lambda = ln sum_c exp(lambda_c),   O = sum_c exp(lambda_c - Lambda) O_c.
+    The largest lambda is subtracted first to keep exp() finite. Chunks with
+    lambda = -inf carry no weight; if every chunk is empty, O = 0, LSE = -inf.
+    part_o [..., n, d], part_lse [..., n] -> O [..., d], LSE [...].
+    """
+    mx = part_lse.max(axis=-1)
+    finite = np.isfinite(mx)
+    safe = np.where(finite, mx, 0.0)
+    w = np.exp(part_lse - safe[..., None])                       # -inf chunks -> 0
+    W = w.sum(axis=-1)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        O = np.where(finite[..., None], (w[..., None] * part_o).sum(axis=-2) / W[..., None], 0.0)
+        LSE = np.where(finite, safe + np.log(W), -np.inf)
+    return O, LSE
