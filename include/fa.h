@@ -1,0 +1,146 @@
+/*
+ * fa.h - exact attention (FlashAttention forward) and split-KV decode for AMD
+ * Instinct MI355X (gfx950). C ABI: plain pointers and sizes only.
+ *
+ * What is computed. For every batch b, query head h and query row i
+ *
+ *     O[b,i,h,:] = sum_{j in A(i)} softmax_j(scale * q_i . k_j) * v_j
+ *     LSE[b,h,i] = ln sum_{j in A(i)} exp(scale * q_i . k_j)
+ *
+ * i.e. softmax(scale * Q K^T) V, evaluated as one fused pass that keeps tiles of
+ * Q on chip, streams K/V tiles through on-chip memory and never writes the
+ * score matrix to device memory ("I/O-Aware Kernels", section FlashAttention;
+ * "FlashAttention & IO-aware attention", Direct answer). The streamed result is
+ * the exact function, up to floating-point rounding order.
+ *
+ * Conventions shared by every entry point
+ *  - Device pointers. Every tensor pointer is a device (HBM) pointer allocated
+ *    by the caller; the library allocates nothing and keeps no per-call state.
+ *  - bf16 tensors are raw 16-bit bfloat16 storage; all tensors are dense and
+ *    contiguous in the stated layout; every pointer must be 16-byte aligned.
+ *  - Head mapping (grouped-query attention): query head h reads KV head
+ *    floor(h * Hkv / Hq); Hq must be a multiple of Hkv.
+ *  - Causal mask (when requested) is aligned bottom-right: row i sees keys
+ *    j <= i + Skv - Sq. A row that sees no key gets O = 0 and LSE = -inf.
+ *  - Arithmetic: bf16 inputs, fp32 scores/softmax/accumulation; O is rounded
+ *    once to bf16 (round-to-nearest-even) at the end. LSE is natural-log fp32.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Every call is
+ *    asynchronous on that stream and never synchronises.
+ *  - Errors: arguments are validated before anything is launched; on a
+ *    validation error nothing runs and a FA_ERR_* code is returned. A failed
+ *    launch returns FA_ERR_HIP. Faults inside a kernel surface at the caller's
+ *    next synchronisation of `stream`. Unsupported head sizes return
+ *    FA_ERR_UNSUPPORTED; there is no fallback path ("FlashAttention &
+ *    IO-aware attention", Interviewer follow-ups: a silent fall-back to a
+ *    materialising path defeats the method).
+ *  - Thread safety: all entry points are reentrant.
+ *  - Results are deterministic run to run (no atomics, fixed split counts).
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,        /* a required pointer is NULL                          */
+  FA_ERR_SHAPE = 2,       /* a size is < 1, Hq % Hkv != 0, or sizes overflow      */
+  FA_ERR_UNSUPPORTED = 3, /* head size not in {64, 128}, or GQA group too large   */
+  FA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                     */
+  FA_ERR_WORKSPACE = 5,   /* decode workspace missing or too small                */
+  FA_ERR_HIP = 6          /* the HIP runtime reported an error at launch          */
+} fa_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* fa_status_string(int status);
+
+/*
+ * fa_fwd - fused exact attention forward ("I/O-Aware Kernels", section
+ * FlashAttention: Q blocks resident, K/V streamed blockwise, online softmax).
+ *
+ *   q   : bf16 [B, Sq,  Hq,  d]     k, v : bf16 [B, Skv, Hkv, d]
+ *   o   : bf16 [B, Sq,  Hq,  d]     (written)
+ *   lse : fp32 [B, Hq, Sq]          (written; may be NULL to skip)
+ *   d in {64, 128}; B, Hq, Hkv, Sq, Skv >= 1; causal is 0 or 1;
+ *   scale multiplies Q K^T before the softmax (1/sqrt(d) in the usual case).
+ * Returns FA_OK or a fa_status error code.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int Hq, int Hkv, int Sq, int Skv, int d,
+           int causal, float scale, void* stream);
+
+/*
+ * fa_fwd_f32out - the same computation as fa_fwd with O written as fp32
+ * [B, Sq, Hq, d] instead of bf16 (no final output rounding). Used to check the
+ * kernel's arithmetic apart from output quantisation; same errors as fa_fwd.
+ */
+int fa_fwd_f32out(const void* q, const void* k, const void* v, float* o, float* lse,
+                  int B, int Hq, int Hkv, int Sq, int Skv, int d,
+                  int causal, float scale, void* stream);
+
+/*
+ * Split-KV decode ("FlashAttention & IO-aware attention", Deep dive and
+ * Interviewer follow-ups: for one query per sequence, split the KV length
+ * across compute units, then merge).
+ *
+ * The Skv keys are cut into num_splits chunks of L = 64 * ceil(ceil(Skv/64) /
+ * num_splits) keys: chunk c covers keys [c*L, min(Skv, (c+1)*L)); trailing
+ * chunks may be empty. Each chunk yields its own normalised output O_c and
+ * log-sum-exp lambda_c; the merge is
+ *     LSE = ln sum_c exp(lambda_c),   O = sum_c exp(lambda_c - LSE) * O_c
+ * (an empty chunk has lambda_c = -inf and weight 0).
+ */
+
+/* Heuristic split count used when num_splits <= 0 (always >= 1). */
+int fa_decode_default_splits(int B, int Hkv, int Skv, int d);
+
+/* Bytes of workspace fa_decode needs for this shape and split count
+ * (num_splits >= 1; pass fa_decode_default_splits(...) for the heuristic's
+ * count). Returns 0 on invalid sizes. */
+size_t fa_decode_workspace_bytes(int B, int Hq, int d, int num_splits);
+
+/*
+ * fa_decode - one decode step: chunk partials, then the merge, both launched on
+ * `stream` (no host synchronisation between them). num_splits <= 0 selects
+ * fa_decode_default_splits(B, Hkv, Skv, d).
+ *   q        : bf16 [B, Hq, d]   (a single query row per sequence and head)
+ *   k_cache, v_cache : bf16 [B, Skv, Hkv, d]  (no mask: every key is visible)
+ *   o        : bf16 [B, Hq, d]   (written)
+ *   lse      : fp32 [B, Hq]      (written; may be NULL)
+ *   workspace: device buffer of at least fa_decode_workspace_bytes(B, Hq, d,
+ *              num_splits) bytes, owned by the caller, 256-byte aligned. It holds
+ *              the fp32 partials [B, Hq, num_splits, d] followed (at the next
+ *              256-byte boundary) by the fp32 chunk LSEs [B, Hq, num_splits].
+ *   Hq / Hkv must be <= 32 (the query heads of one KV head share one tile).
+ */
+int fa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+              int B, int Hq, int Hkv, int Skv, int d, float scale,
+              int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_decode_partials - the first half of fa_decode alone: writes the per-chunk
+ * normalised outputs part_o fp32 [B, Hq, num_splits, d] and chunk LSEs
+ * part_lse fp32 [B, Hq, num_splits]. num_splits must be >= 1.
+ */
+int fa_decode_partials(const void* q, const void* k_cache, const void* v_cache,
+                       float* part_o, float* part_lse,
+                       int B, int Hq, int Hkv, int Skv, int d, float scale,
+                       int num_splits, void* stream);
+
+/*
+ * fa_decode_combine - the merge alone: part_o fp32 [B, Hq, num_splits, d],
+ * part_lse fp32 [B, Hq, num_splits] -> o bf16 [B, Hq, d], lse fp32 [B, Hq]
+ * (lse may be NULL). If every chunk of a row is empty, O = 0 and LSE = -inf.
+ */
+int fa_decode_combine(const float* part_o, const float* part_lse, void* o, float* lse,
+                      int B, int Hq, int d, int num_splits, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,15 @@
+"""Exact FlashAttention forward and split-KV decode for AMD Instinct MI355X (gfx950).
+
+The computation lives in hand-written HIP kernels behind a C ABI (include/fa.h,
+libfa.so). This package is the thin Python binding: it checks tensors, passes
+pointers and the current HIP stream, and raises on any library error. Importing
+it loads libfa.so and fails loudly if the library is not built.
+"""
+from . import _lib
+from .api import (decode, decode_chunk_bounds, decode_combine, decode_default_splits, decode_partials,
+                  decode_workspace_bytes, fwd)
+
+_lib.load()
+
+__all__ = ["fwd", "decode", "decode_partials", "decode_combine", "decode_default_splits",
+           "decode_workspace_bytes", "decode_chunk_bounds"]

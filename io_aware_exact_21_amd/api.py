@@ -1,0 +1,139 @@
+"""Python binding of the attention library: argument marshalling only.
+
+Tensors are torch device tensors (torch supplies device memory and the current
+HIP stream); every step of the computation runs in the library's HIP kernels.
+Names follow the C ABI in include/fa.h.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _lib
+
+
+def _stream_ptr(t: torch.Tensor):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device}); there is no CPU path")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if t.dim() != ndim or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {ndim}-d tensor (got shape {tuple(t.shape)})")
+
+
+def _scale(scale, d: int) -> float:
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False, scale=None,
+        out: torch.Tensor | None = None, lse: torch.Tensor | None = None, return_lse: bool = True,
+        out_f32: bool = False):
+    """Exact attention forward. q [B,Sq,Hq,d], k/v [B,Skv,Hkv,d] bf16 -> (o, lse).
+
+    o has q's shape (bf16, or fp32 with ``out_f32``); lse is fp32 [B,Hq,Sq] (None
+    when ``return_lse`` is False).
+    """
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, torch.bfloat16, 4)
+    B, Sq, Hq, d = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Skv, Hkv, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"k/v shape {tuple(k.shape)}/{tuple(v.shape)} does not match q {tuple(q.shape)}")
+    odt = torch.float32 if out_f32 else torch.bfloat16
+    if out is None:
+        out = torch.empty((B, Sq, Hq, d), dtype=odt, device=q.device)
+    _need(out, "out", odt, 4)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 3)
+    lib = _lib.load()
+    fn = lib.fa_fwd_f32out if out_f32 else lib.fa_fwd
+    st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+            lse.data_ptr() if lse is not None else None,
+            B, Hq, Hkv, Sq, Skv, d, int(bool(causal)), _scale(scale, d), _stream_ptr(q))
+    _lib.check(st, "fa_fwd_f32out" if out_f32 else "fa_fwd")
+    return out, lse
+
+
+def decode_default_splits(B: int, Hkv: int, Skv: int, d: int) -> int:
+    return int(_lib.load().fa_decode_default_splits(B, Hkv, Skv, d))
+
+
+def decode_workspace_bytes(B: int, Hq: int, d: int, num_splits: int) -> int:
+    return int(_lib.load().fa_decode_workspace_bytes(B, Hq, d, num_splits))
+
+
+def decode_chunk_bounds(Skv: int, num_splits: int) -> list:
+    """Key ranges of the decode chunks, as the library cuts them (see include/fa.h)."""
+    tiles = (Skv + 63) // 64
+    L = 64 * ((tiles + num_splits - 1) // num_splits)
+    return [min(Skv, c * L) for c in range(num_splits)] + [Skv]
+
+
+def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, scale=None,
+           num_splits: int = 0, workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
+           lse: torch.Tensor | None = None):
+    """Split-KV decode. q [B,Hq,d], caches [B,Skv,Hkv,d] bf16 -> (o [B,Hq,d] bf16, lse [B,Hq] fp32)."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    B, Hq, d = q.shape
+    Skv, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if tuple(k_cache.shape) != (B, Skv, Hkv, d) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache/v_cache shape does not match q")
+    ns = num_splits if num_splits > 0 else decode_default_splits(B, Hkv, Skv, d)
+    need = decode_workspace_bytes(B, Hq, d, ns)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.bfloat16, 3)
+    _need(lse, "lse", torch.float32, 2)
+    st = _lib.load().fa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(),
+                               lse.data_ptr(), B, Hq, Hkv, Skv, d, _scale(scale, d), ns,
+                               workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                               _stream_ptr(q))
+    _lib.check(st, "fa_decode")
+    return out, lse
+
+
+def decode_partials(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, num_splits: int,
+                    scale=None):
+    """Chunk partials only: (part_o fp32 [B,Hq,n,d], part_lse fp32 [B,Hq,n])."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    B, Hq, d = q.shape
+    Skv, Hkv = k_cache.shape[1], k_cache.shape[2]
+    part_o = torch.empty((B, Hq, num_splits, d), dtype=torch.float32, device=q.device)
+    part_lse = torch.empty((B, Hq, num_splits), dtype=torch.float32, device=q.device)
+    st = _lib.load().fa_decode_partials(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                        part_o.data_ptr(), part_lse.data_ptr(), B, Hq, Hkv, Skv, d,
+                                        _scale(scale, d), num_splits, _stream_ptr(q))
+    _lib.check(st, "fa_decode_partials")
+    return part_o, part_lse
+
+
+def decode_combine(part_o: torch.Tensor, part_lse: torch.Tensor):
+    """Merge chunk partials: part_o [B,Hq,n,d], part_lse [B,Hq,n] fp32 -> (o bf16 [B,Hq,d], lse [B,Hq])."""
+    _need(part_o, "part_o", torch.float32, 4)
+    _need(part_lse, "part_lse", torch.float32, 3)
+    B, Hq, n, d = part_o.shape
+    if tuple(part_lse.shape) != (B, Hq, n):
+        raise ValueError("part_lse shape does not match part_o")
+    out = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=part_o.device)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=part_o.device)
+    st = _lib.load().fa_decode_combine(part_o.data_ptr(), part_lse.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                       B, Hq, d, n, _stream_ptr(part_o))
+    _lib.check(st, "fa_decode_combine")
+    return out, lse

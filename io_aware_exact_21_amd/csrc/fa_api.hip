@@ -1,0 +1,201 @@
+// C ABI of the attention library: argument validation, then one launch per step on the
+// caller's stream. Nothing here allocates memory or synchronises.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "fa.h"
+#include "fa_launch.hpp"
+
+namespace {
+
+constexpr unsigned kQsignMask = 0x80008000u;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_common(int B, int Hq, int Hkv, int Sq, int Skv, int d) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Skv < 1) return FA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  // element counts must stay well inside int64 and row indices inside int32
+  const double q_elems = (double)B * Sq * Hq * d;
+  const double kv_elems = (double)B * Skv * Hkv * d;
+  if (q_elems > 4.0e18 || kv_elems > 4.0e18) return FA_ERR_SHAPE;
+  if ((double)B * Sq > 2.0e9 || (double)B * Skv * Hkv > 2.0e9 || (double)B * Hq > 2.0e9) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+// The kernels need a positive exponent factor c = |scale| * log2(e). A negative scale
+// is folded into Q by flipping its sign bits (exact in bf16). With scale == 0 every
+// score is exactly 0, which is what a zeroed Q gives for any c, so Q is masked to 0.
+int scale_terms(float scale, float* c, unsigned* qsign, unsigned* qmask) {
+  if (!isfinite(scale)) return FA_ERR_SHAPE;
+  *c = scale == 0.f ? 1.f : fabsf(scale) * 1.4426950408889634f;
+  *qsign = scale < 0.f ? kQsignMask : 0u;
+  *qmask = scale == 0.f ? 0u : 0xFFFFFFFFu;
+  return FA_OK;
+}
+
+int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+             int Sq, int Skv, int d, int causal, float scale, void* stream, bool out_f32) {
+  if (!q || !k || !v || !o) return FA_ERR_NULL;
+  int st = check_common(B, Hq, Hkv, Sq, Skv, d);
+  if (st != FA_OK) return st;
+  if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)))
+    return FA_ERR_ALIGN;
+  fa::FwdParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = o;
+  p.lse = lse;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Sq = Sq; p.Skv = Skv; p.d = d;
+  st = scale_terms(scale, &p.c, &p.qsign, &p.qmask);
+  if (st != FA_OK) return st;
+  if (fa::fwd_grid_size(B, Hq, Sq) > 0x7fffffffLL) return FA_ERR_SHAPE;
+  (void)hipGetLastError();
+  if (fa::launch_fwd(p, causal != 0, out_f32, static_cast<hipStream_t>(stream)) != hipSuccess) return FA_ERR_HIP;
+  return FA_OK;
+}
+
+int split_chunk(int Skv, int nsplit) {
+  const int tiles = (Skv + fa::kSplitAlign - 1) / fa::kSplitAlign;
+  return fa::kSplitAlign * ((tiles + nsplit - 1) / nsplit);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int decode_args(const void* q, const void* k, const void* v, int B, int Hq, int Hkv, int Skv, int d,
+                int nsplit) {
+  if (!q || !k || !v) return FA_ERR_NULL;
+  int st = check_common(B, Hq, Hkv, 1, Skv, d);
+  if (st != FA_OK) return st;
+  if (Hq / Hkv > 32) return FA_ERR_UNSUPPORTED;
+  if (nsplit < 1 || (double)B * Hkv * nsplit > 2.0e9) return FA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return FA_ERR_ALIGN;
+  return FA_OK;
+}
+
+int combine_impl(const float* part_o, const float* part_lse, void* o, float* lse, int B, int Hq, int d,
+                 int nsplit, hipStream_t stream) {
+  fa::CombineParams c;
+  c.part_o = part_o;
+  c.part_lse = part_lse;
+  c.o = static_cast<uint16_t*>(o);
+  c.lse = lse;
+  c.rows = B * Hq;
+  c.d = d;
+  c.nsplit = nsplit;
+  (void)hipGetLastError();
+  if (fa::launch_decode_combine(c, stream) != hipSuccess) return FA_ERR_HIP;
+  return FA_OK;
+}
+
+int partials_impl(const void* q, const void* k, const void* v, float* part_o, float* part_lse, int B, int Hq,
+                  int Hkv, int Skv, int d, float scale, int nsplit, hipStream_t stream) {
+  fa::DecParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.part_o = part_o;
+  p.part_lse = part_lse;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Skv = Skv; p.d = d;
+  p.nsplit = nsplit;
+  p.chunk = split_chunk(Skv, nsplit);
+  int st = scale_terms(scale, &p.c, &p.qsign, &p.qmask);
+  if (st != FA_OK) return st;
+  (void)hipGetLastError();
+  if (fa::launch_decode_partials(p, stream) != hipSuccess) return FA_ERR_HIP;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: invalid sizes, head counts or scale";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head size must be 64 or 128 (decode: Hq/Hkv <= 32)";
+    case FA_ERR_ALIGN: return "FA_ERR_ALIGN: every pointer must be 16-byte aligned";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: decode workspace missing, misaligned or too small";
+    case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime rejected the launch";
+    default: return "unknown fa_status";
+  }
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Sq,
+           int Skv, int d, int causal, float scale, void* stream) {
+  return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, d, causal, scale, stream, false);
+}
+
+int fa_fwd_f32out(const void* q, const void* k, const void* v, float* o, float* lse, int B, int Hq, int Hkv,
+                  int Sq, int Skv, int d, int causal, float scale, void* stream) {
+  return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, d, causal, scale, stream, true);
+}
+
+int fa_decode_default_splits(int B, int Hkv, int Skv, int d) {
+  (void)d;
+  if (B < 1 || Hkv < 1 || Skv < 1) return 1;
+  // Aim for about four workgroups per compute unit (256 CUs) while keeping every
+  // chunk at least 512 keys long.
+  const long long units = (long long)B * Hkv;
+  long long want = (4LL * 256 + units - 1) / units;
+  long long most = (Skv + 511) / 512;
+  if (want > most) want = most;
+  if (want > 64) want = 64;
+  if (want < 1) want = 1;
+  return (int)want;
+}
+
+size_t fa_decode_workspace_bytes(int B, int Hq, int d, int num_splits) {
+  if (B < 1 || Hq < 1 || d < 1) return 0;
+  if (num_splits <= 0) return 0;
+  const size_t rows = (size_t)B * Hq * num_splits;
+  return align256(rows * d * sizeof(float)) + align256(rows * sizeof(float));
+}
+
+int fa_decode_partials(const void* q, const void* k_cache, const void* v_cache, float* part_o, float* part_lse,
+                       int B, int Hq, int Hkv, int Skv, int d, float scale, int num_splits, void* stream) {
+  int st = decode_args(q, k_cache, v_cache, B, Hq, Hkv, Skv, d, num_splits);
+  if (st != FA_OK) return st;
+  if (!part_o || !part_lse) return FA_ERR_NULL;
+  if (!aligned16(part_o) || !aligned16(part_lse)) return FA_ERR_ALIGN;
+  return partials_impl(q, k_cache, v_cache, part_o, part_lse, B, Hq, Hkv, Skv, d, scale, num_splits,
+                       static_cast<hipStream_t>(stream));
+}
+
+int fa_decode_combine(const float* part_o, const float* part_lse, void* o, float* lse, int B, int Hq, int d,
+                      int num_splits, void* stream) {
+  if (!part_o || !part_lse || !o) return FA_ERR_NULL;
+  if (B < 1 || Hq < 1 || num_splits < 1 || (double)B * Hq > 2.0e9) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (!aligned16(part_o) || !aligned16(part_lse) || !aligned16(o) || (lse && !aligned16(lse)))
+    return FA_ERR_ALIGN;
+  return combine_impl(part_o, part_lse, o, lse, B, Hq, d, num_splits, static_cast<hipStream_t>(stream));
+}
+
+int fa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse, int B, int Hq,
+              int Hkv, int Skv, int d, float scale, int num_splits, void* workspace, size_t workspace_bytes,
+              void* stream) {
+  if (num_splits <= 0) num_splits = fa_decode_default_splits(B, Hkv, Skv, d);
+  int st = decode_args(q, k_cache, v_cache, B, Hq, Hkv, Skv, d, num_splits);
+  if (st != FA_OK) return st;
+  if (!o) return FA_ERR_NULL;
+  if (!aligned16(o) || (lse && !aligned16(lse))) return FA_ERR_ALIGN;
+  const size_t need = fa_decode_workspace_bytes(B, Hq, d, num_splits);
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || workspace_bytes < need)
+    return FA_ERR_WORKSPACE;
+  float* part_o = static_cast<float*>(workspace);
+  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                             align256((size_t)B * Hq * num_splits * d * sizeof(float)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = partials_impl(q, k_cache, v_cache, part_o, part_lse, B, Hq, Hkv, Skv, d, scale, num_splits, s);
+  if (st != FA_OK) return st;
+  return combine_impl(part_o, part_lse, o, lse, B, Hq, d, num_splits, s);
+}
+
+}  // extern "C"

@@ -1,0 +1,206 @@
+// Split-KV decode for gfx950: one query row per (sequence, query head).
+//
+// A decode step has a single query, so its scores are a 1 x Skv vector and the step
+// is bound by reading the KV cache ("FlashAttention & IO-aware attention", Direct
+// answer and Interviewer follow-ups). To occupy every compute unit the KV length is
+// cut into chunks that run in separate workgroups (Deep dive: FlashDecoding splits
+// the KV length across SMs), each producing a chunk-normalised output and its
+// log-sum-exp; a second kernel merges the chunks by log-sum-exp.
+//
+// The query heads that share one KV head (grouped-query attention, "I/O-Aware
+// Kernels", section FlashAttention) are the columns of one MFMA tile, so every K/V
+// byte is read once for the whole group. Inside a workgroup each wave takes its own
+// 32 keys of every tile; the waves' partial statistics are merged through LDS.
+#include "fa_device.hpp"
+#include "fa_launch.hpp"
+
+namespace fa {
+
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void fa_decode_split_kernel(DecParams p) {
+  constexpr int BCT = 32 * NW;
+  constexpr int NT = NW * 64;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2][2][BCT * D];
+  static_assert(sizeof(smem) >= NW * 32 * (D + 2) * sizeof(float), "merge buffer must fit");
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
+  const int cidx = blockIdx.x % p.nsplit;
+  const int bh = blockIdx.x / p.nsplit;
+  const int b = bh / p.Hkv, hk = bh - b * p.Hkv;
+  const int grp = p.Hq / p.Hkv;                       // query heads per KV head (<= 32)
+  const int c0 = cidx * p.chunk;
+  const int c1 = min(p.Skv, c0 + p.chunk);
+  const int nk = c1 > c0 ? c1 - c0 : 0;
+  const int ntiles = (nk + BCT - 1) / BCT;
+
+  const LaneGeom g = make_geom<D>(lane);
+  const bool real = g.lr < grp;
+  const int h = hk * grp + g.lr;
+
+  u32x4 qop[D / 16];
+  {
+    const uint16_t* qp = p.q + ((int64_t)b * p.Hq + h) * D + 8 * g.hh;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      u32x4 z = {0u, 0u, 0u, 0u};
+      if (real) z = *reinterpret_cast<const u32x4*>(qp + 16 * s);
+      qop[s] = (z ^ p.qsign) & p.qmask;
+    }
+  }
+
+  const int64_t kv_stride = (int64_t)p.Hkv * D;
+  const uint16_t* kb = p.k + ((int64_t)b * p.Skv * p.Hkv + hk) * D;
+  const uint16_t* vb = p.v + ((int64_t)b * p.Skv * p.Hkv + hk) * D;
+
+  f32x16 O[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) O[i] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float c = p.c;
+
+  TileCopy<D, BCT, NT> cp;
+  if (ntiles > 0) {
+    cp.load(kb, vb, kv_stride, c0, c1, tid);
+    cp.store(smem[0][0], smem[0][1], tid);
+  }
+  __syncthreads();
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int k0 = c0 + j * BCT;
+    const bool more = j + 1 < ntiles;
+    if (more) cp.load(kb, vb, kv_stride, k0 + BCT, c1, tid);
+    const uint16_t* ks = smem[j & 1][0];
+    const uint16_t* vs = smem[j & 1][1];
+
+    const int kw = k0 + 32 * w;
+    if (kw < c1) {
+      f32x16 S = scores_block<D>(ks, g, 32 * w, qop);
+      if (kw + 32 > c1) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = kw + 8 * (e >> 2) + 4 * g.hh + (e & 3);
+          if (key >= c1) S[e] = -INFINITY;
+        }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, S[e]);
+      mx = pair_max(mx);
+      const float m_new = fmaxf(m_run, mx * c);
+      const bool need = m_new > m_run + kRescaleGap;
+      if (__ballot(need)) {
+        const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;
+        if (need) m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) O[i] *= alpha;
+      }
+      const float nm = m_run == -INFINITY ? 0.f : -m_run;
+      float ls = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float pe = fast_exp2(fmaf(S[e], c, nm));
+        S[e] = pe;
+        ls += pe;
+      }
+      l_run += ls;
+      pv_step<D>(vs, g, 2 * w, p_operand(S, 0), O);
+      pv_step<D>(vs, g, 2 * w + 1, p_operand(S, 1), O);
+    }
+
+    if (more) cp.store(smem[(j + 1) & 1][0], smem[(j + 1) & 1][1], tid);
+    __syncthreads();
+  }
+
+  // ---- merge the NW waves' partial results through LDS ------------------------------
+  float* mrow = reinterpret_cast<float*>(&smem[0][0][0]);   // [NW][32]
+  float* lrow = mrow + NW * 32;                              // [NW][32]
+  float* obuf = lrow + NW * 32;                              // [NW][32][D]
+  const float l_tot = pair_sum(l_run);
+  if (g.hh == 0) {
+    mrow[w * 32 + g.lr] = m_run;
+    lrow[w * 32 + g.lr] = l_tot;
+  }
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      obuf[(w * 32 + g.lr) * D + 32 * db + 8 * (e >> 2) + 4 * g.hh + (e & 3)] = O[db][e];
+  __syncthreads();
+
+  for (int idx = tid; idx < grp * D; idx += NT) {
+    const int r = idx / D, dim = idx - r * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, mrow[ww * 32 + r]);
+    float lt = 0.f, o = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) {
+        const float sc = fast_exp2(mrow[ww * 32 + r] - M);
+        lt += lrow[ww * 32 + r] * sc;
+        o += obuf[(ww * 32 + r) * D + dim] * sc;
+      }
+    }
+    const int hq = hk * grp + r;
+    const int64_t prow = ((int64_t)b * p.Hq + hq) * p.nsplit + cidx;
+    p.part_o[prow * D + dim] = lt > 0.f ? o / lt : 0.f;
+    if (dim == 0) p.part_lse[prow] = lt > 0.f ? (M + fast_log2(lt)) * kLn2 : -INFINITY;
+  }
+}
+
+// Log-sum-exp merge of the chunk partials; one wave per (sequence, query head).
+template <int D>
+__global__ __launch_bounds__(256) void fa_decode_combine_kernel(CombineParams p) {
+  constexpr int PER = D / 64;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + w;
+  if (row >= p.rows) return;
+  const float* pl = p.part_lse + (int64_t)row * p.nsplit;
+  float M = -INFINITY;
+  for (int c = 0; c < p.nsplit; ++c) M = fmaxf(M, pl[c]);
+  float acc[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) acc[k] = 0.f;
+  float W = 0.f;
+  if (M != -INFINITY) {
+    for (int c = 0; c < p.nsplit; ++c) {
+      const float wc = fast_exp2((pl[c] - M) * kLog2e);
+      W += wc;
+      const float* po = p.part_o + ((int64_t)row * p.nsplit + c) * D + lane * PER;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) acc[k] += wc * po[k];
+    }
+  }
+  const float inv = W > 0.f ? 1.f / W : 0.f;
+  uint16_t* op = p.o + (int64_t)row * D + lane * PER;
+  if (PER == 2) {
+    *reinterpret_cast<unsigned*>(op) = pack_bf16x2(acc[0] * inv, acc[PER - 1] * inv);
+  } else {
+    op[0] = (uint16_t)(pack_bf16x2(acc[0] * inv, 0.f) & 0xFFFFu);
+  }
+  if (p.lse != nullptr && lane == 0) p.lse[row] = W > 0.f ? M + fast_log2(W) * kLn2 : -INFINITY;
+}
+
+hipError_t launch_decode_partials(const DecParams& p, hipStream_t stream) {
+  const long long grid = (long long)p.B * p.Hkv * p.nsplit;
+  if (p.d == 128)
+    hipLaunchKernelGGL((fa_decode_split_kernel<128, kDecWaves>), dim3((unsigned)grid), dim3(kDecWaves * 64), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL((fa_decode_split_kernel<64, kDecWaves>), dim3((unsigned)grid), dim3(kDecWaves * 64), 0,
+                       stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_combine(const CombineParams& p, hipStream_t stream) {
+  const unsigned grid = (unsigned)((p.rows + 3) / 4);
+  if (p.d == 128)
+    hipLaunchKernelGGL((fa_decode_combine_kernel<128>), dim3(grid), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((fa_decode_combine_kernel<64>), dim3(grid), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace fa

@@ -1,0 +1,55 @@
+// Internal launch interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Waves per prefill workgroup (32 query rows each) and per decode-split workgroup
+// (each wave takes 32 keys of every KV tile).
+constexpr int kFwdWaves = 4;
+constexpr int kDecWaves = 2;
+constexpr int kDecTile = 32 * kDecWaves;   // keys per decode KV tile
+constexpr int kSplitAlign = 64;            // decode chunk lengths are multiples of this
+
+struct FwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  void* o;
+  float* lse;
+  int B, Hq, Hkv, Sq, Skv, d;
+  float c;          // |scale| * log2(e), or 1 when scale == 0 (then Q is zeroed)
+  unsigned qsign;   // 0x80008000 when scale < 0 (negates Q exactly), else 0
+  unsigned qmask;   // 0 when scale == 0 (every score is exactly 0), else all ones
+};
+
+struct DecParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  float* part_o;    // [B, Hq, nsplit, d]
+  float* part_lse;  // [B, Hq, nsplit]
+  int B, Hq, Hkv, Skv, d;
+  int nsplit, chunk;  // chunk = keys per split (multiple of kSplitAlign)
+  float c;
+  unsigned qsign;
+  unsigned qmask;
+};
+
+struct CombineParams {
+  const float* part_o;
+  const float* part_lse;
+  uint16_t* o;
+  float* lse;
+  int rows;         // B * Hq
+  int d, nsplit;
+};
+
+long long fwd_grid_size(int B, int Hq, int Sq);
+hipError_t launch_fwd(const FwdParams& p, bool causal, bool out_f32, hipStream_t stream);
+hipError_t launch_decode_partials(const DecParams& p, hipStream_t stream);
+hipError_t launch_decode_combine(const CombineParams& p, hipStream_t stream);
+
+}  // namespace fa

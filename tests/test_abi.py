@@ -1,0 +1,120 @@
+"""The C-ABI library loads on the host, exports every declared symbol, and rejects bad
+arguments before launching anything (these calls never reach the GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from io_aware_exact_21_amd import _lib
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    names = declared_functions()
+    for n in ("fa_fwd", "fa_decode", "fa_decode_combine", "fa_decode_partials", "fa_decode_workspace_bytes",
+              "fa_decode_default_splits", "fa_status_string", "fa_fwd_f32out"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    raw = ctypes.CDLL(lib._name)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_binding_signatures_cover_header(lib):
+    from io_aware_exact_21_amd import _lib
+    assert set(_lib.SIGNATURES) == set(declared_functions())
+
+
+def test_status_strings(lib):
+    for st in range(7):
+        assert lib.fa_status_string(st)
+    assert b"unknown" in lib.fa_status_string(99)
+
+
+A = 1 << 20   # a 16-byte-aligned fake address: never dereferenced, validation fails first
+
+
+def _fwd(lib, q=A, k=A, v=A, o=A, lse=None, B=1, Hq=1, Hkv=1, Sq=4, Skv=4, d=64, causal=0, scale=0.125):
+    return lib.fa_fwd(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, d, causal, scale, None)
+
+
+def test_fwd_validation(lib):
+    from io_aware_exact_21_amd._lib import FA_ERR_ALIGN, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED
+    assert _fwd(lib, q=None) == FA_ERR_NULL
+    assert _fwd(lib, o=None) == FA_ERR_NULL
+    assert _fwd(lib, B=0) == FA_ERR_SHAPE
+    assert _fwd(lib, Sq=0) == FA_ERR_SHAPE
+    assert _fwd(lib, Skv=-3) == FA_ERR_SHAPE
+    assert _fwd(lib, Hq=6, Hkv=4) == FA_ERR_SHAPE
+    assert _fwd(lib, causal=2) == FA_ERR_SHAPE
+    assert _fwd(lib, scale=float("nan")) == FA_ERR_SHAPE
+    assert _fwd(lib, scale=float("inf")) == FA_ERR_SHAPE
+    for d in (32, 80, 96, 256, 0):
+        assert _fwd(lib, d=d) in (FA_ERR_UNSUPPORTED, FA_ERR_SHAPE)
+    assert _fwd(lib, d=96) == FA_ERR_UNSUPPORTED
+    assert _fwd(lib, q=A + 8) == FA_ERR_ALIGN
+    assert _fwd(lib, o=A + 2) == FA_ERR_ALIGN
+    assert _fwd(lib, lse=A + 4) == FA_ERR_ALIGN
+    assert lib.fa_fwd_f32out(A, A, A, A + 4, None, 1, 1, 1, 4, 4, 64, 0, 1.0, None) == FA_ERR_ALIGN
+
+
+def test_decode_validation(lib):
+    from io_aware_exact_21_amd._lib import (FA_ERR_ALIGN, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED,
+                                            FA_ERR_WORKSPACE)
+    need = lib.fa_decode_workspace_bytes(2, 8, 128, 4)
+    assert need == 2 * 8 * 4 * 128 * 4 + 256
+    assert lib.fa_decode_workspace_bytes(0, 8, 128, 4) == 0
+    assert lib.fa_decode_workspace_bytes(2, 8, 128, 0) == 0
+
+    def dec(q=A, o=A, ws=A, wsb=None, Hq=8, Hkv=2, Skv=100, d=128, ns=4):
+        return lib.fa_decode(q, A, A, o, None, 2, Hq, Hkv, Skv, d, 0.1, ns, ws,
+                             need if wsb is None else wsb, None)
+    assert dec(q=None) == FA_ERR_NULL
+    assert dec(o=None) == FA_ERR_NULL
+    assert dec(ws=None) == FA_ERR_WORKSPACE
+    assert dec(wsb=need - 1) == FA_ERR_WORKSPACE
+    assert dec(ws=A + 16) == FA_ERR_WORKSPACE          # workspace must be 256-byte aligned
+    assert dec(Hq=7) == FA_ERR_SHAPE
+    assert dec(Hq=66, Hkv=2) == FA_ERR_UNSUPPORTED     # group of 33 query heads
+    assert dec(d=80) == FA_ERR_UNSUPPORTED
+    assert dec(Skv=0) == FA_ERR_SHAPE
+    assert dec(q=A + 4) == FA_ERR_ALIGN
+    assert lib.fa_decode_partials(A, A, A, None, A, 2, 8, 2, 100, 128, 0.1, 4, None) == FA_ERR_NULL
+    assert lib.fa_decode_partials(A, A, A, A, A, 2, 8, 2, 100, 128, 0.1, 0, None) == FA_ERR_SHAPE
+    assert lib.fa_decode_combine(A, A, None, None, 2, 8, 128, 4, None) == FA_ERR_NULL
+    assert lib.fa_decode_combine(A, A, A, None, 2, 8, 128, 0, None) == FA_ERR_SHAPE
+    assert lib.fa_decode_combine(A, A, A, None, 2, 8, 96, 4, None) == FA_ERR_UNSUPPORTED
+
+
+def test_default_splits_and_chunks(lib):
+    from io_aware_exact_21_amd.api import decode_chunk_bounds
+    assert lib.fa_decode_default_splits(64, 8, 16384, 128) >= 1
+    assert lib.fa_decode_default_splits(1, 1, 100, 128) == 1
+    for Skv, ns in ((16384, 8), (100, 3), (64, 5), (1000, 7), (1, 4)):
+        b = decode_chunk_bounds(Skv, ns)
+        assert b[0] == 0 and b[-1] == Skv and len(b) == ns + 1
+        assert all(b[i] <= b[i + 1] for i in range(ns))
+        assert all(x % 64 == 0 or x == Skv for x in b[:-1])
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    import io_aware_exact_21_amd as fa
+    q = torch.zeros(1, 4, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="no CPU path"):
+        fa.fwd(q, q, q)
