@@ -6,9 +6,9 @@
 
 namespace fa {
 
-// Waves per prefill workgroup (32 query rows each) and per decode-split workgroup
-// (each wave takes 32 keys of every KV tile).
-constexpr int kFwdWaves = 4;
+// Waves per prefill workgroup (32 query rows each, two waves per SIMD) and per
+// decode-split workgroup (each wave takes 32 keys of every KV tile).
+constexpr int kFwdWaves = 8;
 constexpr int kDecWaves = 2;
 constexpr int kDecTile = 32 * kDecWaves;   // keys per decode KV tile
 constexpr int kSplitAlign = 64;            // decode chunk lengths are multiples of this
