@@ -105,6 +105,8 @@ def main() -> int:
     ap.add_argument("--num-splits", type=int, default=0, help="decode splits (0 = library heuristic)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle CPU time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run plain device copies of MIB MiB (reference reading for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
@@ -118,8 +120,20 @@ def main() -> int:
     import io_aware_exact_21_amd as fa
     from synth import WORKLOADS, make_workload
 
-    wf, wd = WORKLOADS[args.fwd_workload], WORKLOADS["decode"]
     dev = torch.device("cuda:0")
+    if args.copy_calibration > 0:
+        # A plain copy of known size: its FETCH_SIZE / WRITE_SIZE readings per dispatch
+        # convert the counters of the attention kernels into bytes.
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "dispatches": 3}))
+        return 0
+
+    wf, wd = WORKLOADS[args.fwd_workload], WORKLOADS["decode"]
 
     def up(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)

@@ -23,47 +23,32 @@ namespace {
 
 constexpr int kFwdTile = 64;      // keys per LDS tile
 constexpr int kFwdStages = 3;     // LDS ring depth (tiles)
+// Bound on the probabilities of the max-free softmax step. A lane's sum of 16
+// probabilities bounds each of them; while it stays at or below 2^64 every p and every
+// fp32 sum of p or p*v stays far inside fp32 and bf16 range (both reach 2^127), so the
+// running max only has to move when a row's scores jump by more than 64 (log2 units).
+constexpr float kRescaleBound = 18446744073709551616.0f;   // 2^64
 
-// One wave-level direct global -> LDS copy: every lane fetches 16 bytes from its own
-// global address and the wave writes them to 64 consecutive 16-byte LDS chunks
-// starting at byte address `lds` (wave-uniform, passed in m0). Issued as inline
-// assembly so that the compiler does not serialise later LDS reads of other ring
-// stages behind it; completion is tracked explicitly with wait_vmcnt + a barrier.
-__device__ __forceinline__ void lds_dma16(const void* gptr, unsigned lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ const lds_u8* lds_ptr(unsigned a) { return (const lds_u8*)(uintptr_t)a; }
+
+// One wave-level direct global -> LDS copy: lane i fetches the 16 bytes at
+// base + voff_i and the wave writes them to 64 consecutive 16-byte LDS chunks starting
+// at byte address `lds` (wave-uniform, passed in m0). Issued as inline assembly so
+// that the compiler does not serialise later LDS reads of other ring stages behind
+// it; completion is tracked explicitly with wait_vmcnt + a barrier. m0 is written
+// only here: no other code in these kernels uses it.
+__device__ __forceinline__ void lds_dma16(const void* base, unsigned voff, unsigned lds) {
+  const unsigned m = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(gptr), "s"(lds)
-               : "memory", "m0");
-}
-
-__device__ __forceinline__ unsigned lds_addr(const uint16_t* p) {
-  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)p;
-}
-
-// Direct global -> LDS copy of one K tile and one V tile (bf16, BCT keys x D) into
-// one ring stage. The lane that fills LDS chunk (key, c) fetches global chunk
-// c ^ swz(key), which stores the tile row-major with the XOR swizzle the operand
-// reads expect. Keys at or past `kmax` re-read key kmax - 1 (finite data that the
-// softmax masks to weight 0).
-template <int D, int BCT, int NW>
-__device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ vb,
-                                         int64_t row_stride, int k0, int kmax, const uint16_t* ks,
-                                         const uint16_t* vs, int w, int lane) {
-  constexpr int CPR = D / 8;              // 16-byte chunks per key row
-  constexpr int KPI = 64 / CPR;           // keys per wave-level copy
-  constexpr int NI = BCT / KPI;           // copies per tensor and tile
-  static_assert(NI % NW == 0, "copies must split evenly over the waves");
-  const int kl = lane / CPR, cl = lane % CPR;
-  const unsigned ka = lds_addr(ks), va = lds_addr(vs);
-#pragma unroll
-  for (int n = 0; n < NI / NW; ++n) {
-    const int i = w + NW * n;
-    const int key = KPI * i + kl;
-    const int kg = min(k0 + key, kmax - 1);
-    const int64_t roff = (int64_t)kg * row_stride;
-    lds_dma16(kb + roff + ((cl ^ k_swz<D>(key)) << 3), ka + i * 1024);
-    lds_dma16(vb + roff + ((cl ^ v_swz<D>(key)) << 3), va + i * 1024);
-  }
+               : "v"(voff), "s"(base), "s"(m)
+               : "memory");
 }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
@@ -73,36 +58,122 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// S^T = K Q^T for one 32-key unit (kr0 = first key row of the unit in the tile).
+// LDS ring: the NS K tiles first, then the NS V tiles (BCT keys x D bf16 each, row-major,
+// 16-byte chunks XOR-swizzled by key). Keeping K and V apart keeps every operand read
+// within a 16-bit immediate of one per-lane base address.
+template <int D, int BCT, int NS>
+struct Ring {
+  static constexpr unsigned kTileBytes = BCT * D * 2;
+  static constexpr unsigned kVBase = NS * kTileBytes;
+  static constexpr unsigned kBytes = 2 * NS * kTileBytes;
+};
+
+// Direct global -> LDS copies of one K tile and one V tile into one ring stage. The
+// lane that fills LDS chunk (key, c) fetches global chunk c ^ swz(key). The tile
+// base is wave-uniform (SGPRs); per-lane byte offsets within a tile are fixed. Keys
+// at or past `kmax` (only in the last tile) re-read key kmax - 1: finite data that the
+// softmax gives weight 0.
+template <int D, int BCT, int NW, int NS>
+struct KvDma {
+  static constexpr int CPR = D / 8;              // 16-byte chunks per key row
+  static constexpr int KPI = 64 / CPR;           // keys per wave-level copy
+  static constexpr int NI = BCT / KPI;           // copies per tensor and tile
+  static constexpr int NPW = NI / NW;            // copies per wave, tensor and tile
+  static_assert(NI % NW == 0, "copies must split evenly over the waves");
+  unsigned koff[NPW], voff[NPW];                 // byte offsets within a tile
+
+  __device__ __forceinline__ static int key_of(int n, int w, int lane) { return KPI * (w + NW * n) + lane / CPR; }
+
+  __device__ __forceinline__ void init(int64_t row_stride, int w, int lane) {
+    const int cl = lane % CPR;
+#pragma unroll
+    for (int n = 0; n < NPW; ++n) {
+      const int key = key_of(n, w, lane);
+      koff[n] = (unsigned)(key * row_stride * 2) + ((cl ^ k_swz<D>(key)) << 4);
+      voff[n] = (unsigned)(key * row_stride * 2) + ((cl ^ v_swz<D>(key)) << 4);
+    }
+  }
+
+  // Copy tile t (keys t*BCT ...) into ring stage t % NS.
+  __device__ __forceinline__ void issue(const uint16_t* kb, const uint16_t* vb, int64_t row_stride, int t,
+                                        int kmax, unsigned ring, int w, int lane) const {
+    using R = Ring<D, BCT, NS>;
+    const int k0 = t * BCT;
+    const unsigned kst = ring + (unsigned)(t % NS) * R::kTileBytes;
+    const unsigned vst = kst + R::kVBase;
+    const uint16_t* kt = kb + (int64_t)k0 * row_stride;
+    const uint16_t* vt = vb + (int64_t)k0 * row_stride;
+    if (k0 + BCT <= kmax) {
+#pragma unroll
+      for (int n = 0; n < NPW; ++n) {
+        lds_dma16(kt, koff[n], kst + (w + NW * n) * 1024);
+        lds_dma16(vt, voff[n], vst + (w + NW * n) * 1024);
+      }
+    } else {
+      const int cl = lane % CPR;
+#pragma unroll
+      for (int n = 0; n < NPW; ++n) {
+        const int key = key_of(n, w, lane);
+        const unsigned roff = (unsigned)((int64_t)min(key, kmax - 1 - k0) * row_stride * 2);
+        lds_dma16(kt, roff + ((cl ^ k_swz<D>(key)) << 4), kst + (w + NW * n) * 1024);
+        lds_dma16(vt, roff + ((cl ^ v_swz<D>(key)) << 4), vst + (w + NW * n) * 1024);
+      }
+    }
+  }
+};
+
+// S^T = K Q^T for one 32-key unit. `ka[st]` + `imm` = LDS byte address of this lane's K
+// operand chunk for 16-dim step st; `imm` selects the ring stage and the unit's rows.
 template <int D>
-__device__ __forceinline__ f32x16 qk_unit(const uint16_t* ks, const LaneGeom& g, int kr0,
-                                          const u32x4 (&q)[D / 16]) {
+__device__ __forceinline__ f32x16 qk_unit(const unsigned (&ka)[D / 16], unsigned imm, const u32x4 (&q)[D / 16]) {
   f32x16 s = {};
 #pragma unroll
   for (int st = 0; st < D / 16; ++st) {
-    const u32x4 a = *reinterpret_cast<const u32x4*>(ks + kr0 * D + g.kbase[st]);
+    const u32x4 a = *reinterpret_cast<const lds_u32x4*>(lds_ptr(ka[st]) + imm);
     s = mfma_32x32x16(a, q[st], s);
   }
   return s;
 }
 
-// O^T += V^T P^T for one 32-key unit (two 16-key steps starting at step t0 of the tile).
+// O^T += V^T P^T for one 32-key unit: two 16-key steps, D/32 dim blocks. `va[db]` +
+// `imm` = LDS byte address of this lane's transposing-read origin for dim block db at
+// the unit's first 16-key step.
 template <int D>
-__device__ __forceinline__ void pv_unit(const uint16_t* vs, const LaneGeom& g, int t0, const u32x4 (&pp)[2],
+__device__ __forceinline__ void pv_unit(const unsigned (&va)[D / 32], unsigned imm, const u32x4 (&pp)[2],
                                         f32x16 (&o)[D / 32]) {
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      const uint16_t* a0p = vs + (16 * (t0 + tt)) * D + g.vbase[db];
+      const lds_u8* a0p = lds_ptr(va[db]) + imm + tt * 16 * D * 2;
       const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0p));
-      const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0p + 8 * D));
+      const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0p + 8 * D * 2));
       const u32x2 x0 = __builtin_bit_cast(u32x2, r0), x1 = __builtin_bit_cast(u32x2, r1);
       const u32x4 a = {x0[0], x0[1], x1[0], x1[1]};
       o[db] = mfma_32x32x16(a, pp[tt], o[db]);
     }
   }
 }
+
+// Interleave of one slot (P.V of one unit, Q.K^T of a later unit, softmax of the unit
+// in between): every MFMA is followed by the next operand reads and a share of the
+// softmax VALU work. Scheduling hints only; they do not change what is computed.
+#define FA_SG(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
+#define FA_SG_MFMA 0x008
+#define FA_SG_DSRD 0x100
+#define FA_SG_VALU 0x402   // VALU incl. transcendentals
+#define FA_SG_STEP(nrd, nv) FA_SG(FA_SG_MFMA, 1); FA_SG(FA_SG_DSRD, nrd); FA_SG(FA_SG_VALU, nv)
+template <int D>
+__device__ __forceinline__ void slot_schedule() {
+  FA_SG(FA_SG_DSRD, 4);
+  FA_SG_STEP(2, 4); FA_SG_STEP(2, 4); FA_SG_STEP(2, 4); FA_SG_STEP(2, 4);
+  FA_SG_STEP(2, 4); FA_SG_STEP(2, 4); FA_SG_STEP(1, 4); FA_SG_STEP(1, 4);
+  if (D == 128) {
+    FA_SG_STEP(1, 4); FA_SG_STEP(1, 4); FA_SG_STEP(1, 4); FA_SG_STEP(1, 4);
+    FA_SG_STEP(1, 4); FA_SG_STEP(1, 4); FA_SG_STEP(0, 4); FA_SG_STEP(0, 4);
+  }
+}
+#undef FA_SG_STEP
 
 __device__ __forceinline__ unsigned bf16_pair_sum_weights() { return 0x3F803F80u; }   // (1.0, 1.0)
 
@@ -147,6 +218,137 @@ __device__ __forceinline__ void softmax_unit(f32x16 s, float& m, float& l, float
   l = fmaf(l, alpha, ls);
 }
 
+// Softmax step without a max reduction, for units whose row already has a finite
+// running max m: p = 2^(s*c - m) packed to bf16, and this lane's sum of the rounded p in
+// `ls`. Every p is <= kRescaleBound whenever ls is, so the caller only has to redo the
+// unit with the full step (which may move m) when some lane's ls exceeds that bound;
+// the result is then the same as taking the full step directly.
+__device__ __forceinline__ void softmax_unit_nomax(const f32x16& s, float m, u32x4 (&pout)[2], float c,
+                                                   float& ls) {
+  const float nm = -m;
+  ls = 0.f;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    unsigned pk[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float a = fast_exp2(fmaf(s[8 * h + 2 * i], c, nm));
+      const float b = fast_exp2(fmaf(s[8 * h + 2 * i + 1], c, nm));
+      pk[i] = pack_bf16x2(a, b);
+      ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[i]),
+                                           __builtin_bit_cast(bf16x2, bf16_pair_sum_weights()), ls, false);
+    }
+    pout[h] = u32x4{pk[0], pk[1], pk[2], pk[3]};
+  }
+}
+
+// Per-wave state of the forward pass and its per-tile steps.
+template <int D, bool CAUSAL>
+struct FwdWave {
+  static constexpr int BCT = kFwdTile;
+  static constexpr int NS = kFwdStages;
+  using R = Ring<D, BCT, NS>;
+
+  u32x4 q[D / 16];            // Q^T operand (this wave's 32 rows)
+  f32x16 o[D / 32];           // O^T accumulator
+  f32x16 s0, s1;              // scores of the even / odd unit in flight
+  u32x4 p0[2], p1[2];         // bf16 probabilities of the even / odd unit
+  float m, l, alpha, c;       // running max (log2 units), normaliser, pending factor, |scale|*log2 e
+  unsigned kb_[D / 16];       // K operand read bases (ring stage 0)
+  unsigned vb_[D / 32];       // V^T operand read bases (ring stage 0)
+  int nu, umask, tmask;       // live units, first masked unit, mask threshold
+
+  __device__ __forceinline__ void softmax_any(const f32x16& sc, u32x4 (&pp)[2], int u) {
+    if (u >= umask) softmax_unit<true>(sc, m, l, alpha, pp, c, tmask - 32 * u);
+    else softmax_unit<false>(sc, m, l, alpha, pp, c, 0);
+  }
+  // Apply the factor of the unit just softmaxed to the accumulator: after the P.V
+  // product of the previous unit, before the next one. Rare: the max moves lazily.
+  __device__ __forceinline__ void rescale() {
+    if (__ballot(alpha != 1.f)) {
+      // element by element: a vector-times-scalar product would splat alpha into a
+      // 16-register vector first
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
+    }
+  }
+
+  // Slot A of tile j (units 2j .. 2j + 3 live, unmasked, finite running max): PV(2j),
+  // QK(2j + 2) and the max-free softmax of unit 2j + 1. Returns false when some row's
+  // probabilities exceed the bound (its max jumped); unit 2j + 1 must then be redone with
+  // redo_a before slot B.
+  __device__ __forceinline__ bool fast_slot_a(const unsigned (&ka)[D / 16], const unsigned (&va)[D / 32]) {
+    float ls;
+    pv_unit<D>(va, 0, p0, o);
+    s0 = qk_unit<D>(ka, 0, q);
+    softmax_unit_nomax(s1, m, p1, c, ls);
+    slot_schedule<D>();
+    if (__ballot(!(ls <= kRescaleBound))) return false;
+    l += ls;
+    return true;
+  }
+  // Slot B of tile j: PV(2j + 1), QK(2j + 3) and the max-free softmax of unit 2j + 2.
+  __device__ __forceinline__ bool fast_slot_b(const unsigned (&ka)[D / 16], const unsigned (&va)[D / 32]) {
+    float ls;
+    pv_unit<D>(va, 32 * D * 2, p1, o);
+    s1 = qk_unit<D>(ka, 32 * D * 2, q);
+    softmax_unit_nomax(s0, m, p0, c, ls);
+    slot_schedule<D>();
+    if (__ballot(!(ls <= kRescaleBound))) return false;
+    l += ls;
+    return true;
+  }
+  // Redo the softmax of a unit with the full step (which moves the running max) and
+  // rescale the accumulator. The unit's scores are formed again from its K tile, still
+  // resident in LDS: the same MFMAs in the same order give bitwise the same scores.
+  __device__ __forceinline__ void redo_unit(const unsigned (&ka)[D / 16], unsigned imm, u32x4 (&pp)[2]) {
+    softmax_unit<false>(qk_unit<D>(ka, imm, q), m, l, alpha, pp, c, 0);
+    rescale();
+  }
+  __device__ __forceinline__ void tile_addrs(int j, unsigned (&ka)[D / 16], unsigned (&va)[D / 32],
+                                             unsigned (&kj)[D / 16]) const {
+    const unsigned kv = (unsigned)(j % NS) * R::kTileBytes;
+    const unsigned kk = (unsigned)((j + 1) % NS) * R::kTileBytes;
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) {
+      ka[i] = kb_[i] + kk;
+      kj[i] = kb_[i] + kv;
+    }
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) va[i] = vb_[i] + kv;
+  }
+
+  // Tile j with per-unit guards (causal diagonal, ragged tail, finished waves).
+  __device__ __forceinline__ void guarded_tile(int j) {
+    const unsigned kv = (unsigned)(j % NS) * R::kTileBytes;
+    const unsigned kk = (unsigned)((j + 1) % NS) * R::kTileBytes;
+    unsigned ka[D / 16], va[D / 32];
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) ka[i] = kb_[i] + kk;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) va[i] = vb_[i] + kv;
+    const int u0 = 2 * j;
+    if (u0 < nu) {
+      pv_unit<D>(va, 0, p0, o);
+      if (u0 + 2 < nu) s0 = qk_unit<D>(ka, 0, q);
+      if (u0 + 1 < nu) {
+        softmax_any(s1, p1, u0 + 1);
+        rescale();
+      }
+    }
+    if (u0 + 1 < nu) {
+      pv_unit<D>(va, 32 * D * 2, p1, o);
+      if (u0 + 3 < nu) s1 = qk_unit<D>(ka, 32 * D * 2, q);
+      if (u0 + 2 < nu) {
+        softmax_any(s0, p0, u0 + 2);
+        rescale();
+      }
+    }
+  }
+};
+
 }  // namespace
 
 template <int D, bool CAUSAL, bool OUT_F32>
@@ -155,8 +357,8 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fa_fwd_kernel(FwdParams p) {
   constexpr int BCT = kFwdTile;
   constexpr int NS = kFwdStages;
   constexpr int BR = 32 * NW;
-  constexpr int TE = BCT * D;                           // bf16 per K (or V) tile
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[NS][2][TE];   // [stage][K|V]
+  using R = Ring<D, BCT, NS>;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[R::kBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -178,126 +380,107 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fa_fwd_kernel(FwdParams p) {
   if (CAUSAL) kend = min(p.Skv, min(p.Sq, q0 + BR) + diag);
   const int ntiles = kend > 0 ? (kend + BCT - 1) / BCT : 0;
 
+  FwdWave<D, CAUSAL> wv;
   const LaneGeom g = make_geom<D>(lane);
+  const unsigned ring = lds_addr(smem);
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) wv.kb_[st] = ring + 2u * g.kbase[st];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) wv.vb_[db] = ring + R::kVBase + 2u * g.vbase[db];
+
   const int row_lo = q0 + 32 * w;                      // first query row of this wave
   const int row_hi = min(row_lo + 31, p.Sq - 1);       // last real row of this wave
   // keys this wave needs, in 32-key units
   int kw = row_lo < p.Sq ? p.Skv : 0;
   if (CAUSAL && row_lo < p.Sq) kw = max(0, min(p.Skv, row_hi + diag + 1));
-  const int nu = (kw + 31) / 32;
+  wv.nu = (kw + 31) / 32;
   // units [0, umask) need no per-element mask (neither the causal diagonal nor the tail)
   int umask = p.Skv / 32;
   if (CAUSAL) umask = min(umask, row_lo + diag + 1 > 0 ? (row_lo + diag + 1) / 32 : 0);
+  wv.umask = umask;
 
   // ---- Q^T operand, resident in registers --------------------------------------------
   const int qrow = row_lo + g.lr;
-  u32x4 q[D / 16];
   {
     const uint16_t* qp = p.q + ((int64_t)(b * p.Sq + qrow) * p.Hq + h) * D + 8 * g.hh;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
       u32x4 z = {0u, 0u, 0u, 0u};
       if (qrow < p.Sq) z = *reinterpret_cast<const u32x4*>(qp + 16 * s);
-      q[s] = (z ^ p.qsign) & p.qmask;                  // the sign of the scale is folded into Q
+      wv.q[s] = (z ^ p.qsign) & p.qmask;               // the sign of the scale is folded into Q
     }
   }
-  // unit u masks this lane's key offsets above t - 32u
+  // unit u masks this lane's key offsets above tmask - 32u
   const int lim = CAUSAL ? min(p.Skv - 1, qrow + diag) : p.Skv - 1;
-  const int tmask = lim - 4 * g.hh;
+  wv.tmask = lim - 4 * g.hh;
 
   const int64_t kv_stride = (int64_t)p.Hkv * D;
   const uint16_t* kb = p.k + ((int64_t)b * p.Skv * p.Hkv + hk) * D;
   const uint16_t* vb = p.v + ((int64_t)b * p.Skv * p.Hkv + hk) * D;
+  KvDma<D, BCT, NW, NS> dma;
+  dma.init(kv_stride, w, lane);
 
-  f32x16 o[D / 32];
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) o[i] = f32x16{};
-  float m = -INFINITY, l = 0.f, alpha = 1.f;
-  const float c = p.c;
-
-  f32x16 s0, s1;               // scores of the even / odd unit in flight
-  u32x4 p0[2], p1[2];          // bf16 probabilities of the even / odd unit
+  for (int i = 0; i < D / 32; ++i) wv.o[i] = f32x16{};
+  wv.m = -INFINITY;
+  wv.l = 0.f;
+  wv.alpha = 1.f;
+  wv.c = p.c;
 
   // ---- prologue: tiles 0 and 1 resident, then Q.K^T of units 0, 1 and softmax of 0 --
-  if (ntiles > 0) dma_tile<D, BCT, NW>(kb, vb, kv_stride, 0, p.Skv, smem[0][0], smem[0][1], w, lane);
-  if (ntiles > 1) dma_tile<D, BCT, NW>(kb, vb, kv_stride, BCT, p.Skv, smem[1][0], smem[1][1], w, lane);
+  if (ntiles > 0) dma.issue(kb, vb, kv_stride, 0, p.Skv, ring, w, lane);
+  if (ntiles > 1) dma.issue(kb, vb, kv_stride, 1, p.Skv, ring, w, lane);
   wait_vmcnt<0>();     // iteration 0 reads K of tile 1 already
   __syncthreads();
 
-  auto softmax_any = [&](const f32x16& sc, u32x4 (&pp)[2], int u) {
-    if (u >= umask) softmax_unit<true>(sc, m, l, alpha, pp, c, tmask - 32 * u);
-    else softmax_unit<false>(sc, m, l, alpha, pp, c, 0);
-  };
-  // Apply the factor of the unit just softmaxed to the accumulator: after the P.V
-  // product of the previous unit, before the next one. Rare: the max moves lazily.
-  auto rescale = [&]() {
-    if (__ballot(alpha != 1.f)) {
-#pragma unroll
-      for (int i = 0; i < D / 32; ++i) o[i] *= alpha;
-    }
-  };
-
-  if (nu > 0) {
-    s0 = qk_unit<D>(smem[0][0], g, 0, q);
-    if (nu > 1) s1 = qk_unit<D>(smem[0][0], g, 32, q);
-    softmax_any(s0, p0, 0);    // o is zero here, so unit 0's factor needs no application
+  if (wv.nu > 0) {
+    wv.s0 = qk_unit<D>(wv.kb_, 0, wv.q);
+    if (wv.nu > 1) wv.s1 = qk_unit<D>(wv.kb_, 32 * D * 2, wv.q);
+    wv.softmax_any(wv.s0, wv.p0, 0);    // o is zero here, so unit 0's factor needs no application
   }
 
   // ---- main loop: one tile (two units) per iteration ------------------------------
-  // Tiles [0, jf) have all four pipeline units live and unmasked for this wave and run
-  // without guards; the rest (causal diagonal, ragged tail, finished waves) run guarded.
+  // Tiles [0, jf) have all four pipeline units live and unmasked for this wave (and a
+  // finite running max, set by unit 0) and run without guards; the rest run guarded.
   // Every wave passes the same number of barriers.
-  int jf = min(nu - 3, umask - 2);
+  int jf = min(wv.nu - 3, umask - 2);
   jf = jf > 0 ? min((jf + 1) / 2, ntiles) : 0;
   int j = 0;
-  for (; j < jf; ++j) {
-    if (j + 2 < ntiles) {
-      const int st2 = (j + 2) % NS;
-      dma_tile<D, BCT, NW>(kb, vb, kv_stride, (j + 2) * BCT, p.Skv, smem[st2][0], smem[st2][1], w, lane);
+  while (j < jf) {
+    // hot loop: no guards, no max reductions, no accumulator rescale
+    int stop = 0;
+    for (; j < jf; ++j) {
+      if (j + 2 < ntiles) dma.issue(kb, vb, kv_stride, j + 2, p.Skv, ring, w, lane);
+      unsigned ka[D / 16], va[D / 32], kj[D / 16];
+      wv.tile_addrs(j, ka, va, kj);
+      if (!wv.fast_slot_a(ka, va)) { stop = 1; break; }
+      if (!wv.fast_slot_b(ka, va)) { stop = 2; break; }
+      if (j + 2 < ntiles) wait_vmcnt<0>();
+      __syncthreads();
     }
-    const uint16_t* vs = smem[j % NS][1];
-    const uint16_t* ks1 = smem[(j + 1) % NS][0];
-    pv_unit<D>(vs, g, 0, p0, o);                  // PV(2j)
-    s0 = qk_unit<D>(ks1, g, 0, q);                // QK(2j + 2)
-    softmax_unit<false>(s1, m, l, alpha, p1, c, 0);   // softmax(2j + 1)
-    rescale();
-    pv_unit<D>(vs, g, 2, p1, o);                  // PV(2j + 1)
-    s1 = qk_unit<D>(ks1, g, 32, q);               // QK(2j + 3)
-    softmax_unit<false>(s0, m, l, alpha, p0, c, 0);   // softmax(2j + 2)
-    rescale();
+    if (stop == 0) break;
+    // A row max jumped inside tile j: redo that unit, finish the tile, resume.
+    unsigned ka[D / 16], va[D / 32], kj[D / 16];
+    wv.tile_addrs(j, ka, va, kj);
+    if (stop == 1) {
+      wv.redo_unit(kj, 32 * D * 2, wv.p1);                    // unit 2j + 1
+      if (!wv.fast_slot_b(ka, va)) wv.redo_unit(ka, 0, wv.p0);  // unit 2j + 2
+    } else {
+      wv.redo_unit(ka, 0, wv.p0);                             // unit 2j + 2
+    }
     if (j + 2 < ntiles) wait_vmcnt<0>();
     __syncthreads();
+    ++j;
   }
   for (; j < ntiles; ++j) {
-    if (j + 2 < ntiles) {
-      const int st2 = (j + 2) % NS;
-      dma_tile<D, BCT, NW>(kb, vb, kv_stride, (j + 2) * BCT, p.Skv, smem[st2][0], smem[st2][1], w, lane);
-    }
-    const uint16_t* vs = smem[j % NS][1];
-    const uint16_t* ks1 = smem[(j + 1) % NS][0];
-    const int u0 = 2 * j;
-    if (u0 < nu) {
-      pv_unit<D>(vs, g, 0, p0, o);
-      if (u0 + 2 < nu) s0 = qk_unit<D>(ks1, g, 0, q);
-      if (u0 + 1 < nu) {
-        softmax_any(s1, p1, u0 + 1);
-        rescale();
-      }
-    }
-    if (u0 + 1 < nu) {
-      pv_unit<D>(vs, g, 2, p1, o);
-      if (u0 + 3 < nu) s1 = qk_unit<D>(ks1, g, 32, q);
-      if (u0 + 2 < nu) {
-        softmax_any(s0, p0, u0 + 2);
-        rescale();
-      }
-    }
+    if (j + 2 < ntiles) dma.issue(kb, vb, kv_stride, j + 2, p.Skv, ring, w, lane);
+    wv.guarded_tile(j);
     if (j + 2 < ntiles) wait_vmcnt<0>();
     __syncthreads();
   }
 
   // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l) -------------------------------
-  const float lt = pair_sum(l);
+  const float lt = pair_sum(wv.l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (qrow < p.Sq) {
     const int64_t obase = ((int64_t)(b * p.Sq + qrow) * p.Hq + h) * D;
@@ -306,8 +489,8 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fa_fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int dim = 32 * db + 8 * i + 4 * g.hh;
-        const float o0 = o[db][4 * i + 0] * inv, o1 = o[db][4 * i + 1] * inv;
-        const float o2 = o[db][4 * i + 2] * inv, o3 = o[db][4 * i + 3] * inv;
+        const float o0 = wv.o[db][4 * i + 0] * inv, o1 = wv.o[db][4 * i + 1] * inv;
+        const float o2 = wv.o[db][4 * i + 2] * inv, o3 = wv.o[db][4 * i + 3] * inv;
         if (OUT_F32) {
           float4 v4 = make_float4(o0, o1, o2, o3);
           *reinterpret_cast<float4*>(static_cast<float*>(p.o) + obase + dim) = v4;
@@ -317,7 +500,7 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fa_fwd_kernel(FwdParams p) {
         }
       }
     if (p.lse != nullptr && g.hh == 0)
-      p.lse[(int64_t)(b * p.Hq + h) * p.Sq + qrow] = lt > 0.f ? (m + fast_log2(lt)) * kLn2 : -INFINITY;
+      p.lse[(int64_t)(b * p.Hq + h) * p.Sq + qrow] = lt > 0.f ? (wv.m + fast_log2(lt)) * kLn2 : -INFINITY;
   }
 }
 
