@@ -364,12 +364,28 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fa_fwd_kernel(FwdParams p) {
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: per-wave branches stay scalar
 
-  // ---- work unit: heaviest causal tiles first; whole heads kept on one XCD ----------
+  // ---- work unit ------------------------------------------------------------------
+  // Workgroups are dealt to the 8 XCDs round-robin (block i runs on XCD i % 8). Each
+  // XCD gets whole heads, so their K/V stay in that XCD's L2, and walks its share
+  // heaviest query tiles first across all of its heads (largest-first scheduling keeps
+  // the causal tail short). Shapes that do not split evenly use one global
+  // heaviest-first order.
   const int n_qt = (p.Sq + BR - 1) / BR;
   const int total = p.B * p.Hq * n_qt;
-  int L = blockIdx.x;
-  if ((total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);
-  const int hl = L / n_qt, rr = L - hl * n_qt;
+  int hl, rr;
+  {
+    const int L = blockIdx.x;
+    const int heads = p.B * p.Hq;
+    if ((total & 7) == 0 && ((total >> 3) % n_qt) == 0) {
+      const int hpx = (total >> 3) / n_qt;          // heads per XCD
+      const int li = L >> 3;
+      rr = li / hpx;
+      hl = (L & 7) * hpx + (li - rr * hpx);
+    } else {
+      rr = L / heads;
+      hl = L - rr * heads;
+    }
+  }
   const int qt = CAUSAL ? (n_qt - 1 - rr) : rr;
   const int b = hl / p.Hq, h = hl - b * p.Hq;
   const int hk = (h * p.Hkv) / p.Hq;
