@@ -26,7 +26,10 @@ METRIC = "fwd attention TFLOP/s (bf16, causal-adjusted) & % MFMA peak; decode HB
 PEAK_MFMA_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0              # MI355X HBM3E
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["fa_device.hpp", "fa_fwd.hip", "fa_decode.hip", "fa_launch.hpp"]
+# Sources each kernel family is built from: an HBM-traffic record is used only while
+# the sources it was measured on are unchanged.
+KERNEL_SOURCES = {"fwd": ["fa_device.hpp", "fa_launch.hpp", "fa_fwd.hip"],
+                  "decode": ["fa_device.hpp", "fa_launch.hpp", "fa_decode.hip"]}
 
 
 def fwd_flops(w) -> float:
@@ -46,23 +49,23 @@ def decode_bytes(w) -> dict:
     return {"total": kv + q + q + w.B * w.Hq * 4, "split_kernel": kv + q}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(family: str) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[family]:
         with open(os.path.join(ROOT, "io_aware_exact_21_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(name: str):
-    """HBM bytes per launch from the committed PMC summary, if taken on the current kernels."""
+def measured_traffic(name: str, family: str):
+    """HBM bytes per launch from the committed PMC summary, if taken on the current kernel sources."""
     path = os.path.join(PROFILES, name)
     try:
         with open(path) as f:
             rec = json.loads(next(l for l in f if l.startswith("{")))
     except (OSError, StopIteration, ValueError):
         return None
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash(family):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -198,8 +201,8 @@ def main() -> int:
     dec_gbs = db["total"] / ((split_ms + comb_ms) * 1e-3) / 1e9
     split_gbs = db["split_kernel"] / (split_ms * 1e-3) / 1e9
 
-    t_fwd = measured_traffic(f"fa_fwd_{args.fwd_workload}_hbm_traffic.txt")
-    t_dec = measured_traffic("fa_decode_split_decode_hbm_traffic.txt")
+    t_fwd = measured_traffic(f"fa_fwd_{args.fwd_workload}_hbm_traffic.txt", "fwd")
+    t_dec = measured_traffic("fa_decode_split_decode_hbm_traffic.txt", "decode")
     rec = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(total_ms / args.steps, 4),
@@ -219,7 +222,7 @@ def main() -> int:
             "combine_kernel_ms": round(comb_ms, 4), "algorithmic_bytes": db["total"],
         },
         "wall_s_timed": round(t_wall, 3),
-        "kernel_source_hash": kernel_source_hash(),
+        "kernel_source_hash": {f: kernel_source_hash(f) for f in KERNEL_SOURCES},
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
