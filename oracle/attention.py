@@ -211,3 +211,32 @@ def combine_ref(part_o: np.ndarray, part_lse: np.ndarray):
         O = np.where(finite[..., None], (w[..., None] * part_o).sum(axis=-2) / W[..., None], 0.0)
         LSE = np.where(finite, safe + np.log(W), -np.inf)
     return O, LSE
+
+
+def paged_decode_ref(q: np.ndarray, k_pages: np.ndarray, v_pages: np.ndarray, block_table: np.ndarray,
+                     seq_lens: np.ndarray, *, scale: float):
+    """Single-query decode over a paged KV cache.
+
+    [IOP, FlashAttention] mentions paged KV caches; the layout is this library's
+    reading: pools k_pages, v_pages [num_pages, page_size, Hkv, d], and sequence b's
+    token t lives in page block_table[b, t // page_size] at slot t % page_size; the
+    sequence holds seq_lens[b] tokens, all visible to its query. The result is the
+    plain decode over the tokens gathered in order. A sequence with no token gets
+    O = 0 and LSE = -inf.
+    q [B,Hq,d] -> O [B,Hq,d], LSE [B,Hq] (float64).
+    """
+    B, Hq, d = q.shape
+    page_size = k_pages.shape[1]
+    O = np.zeros((B, Hq, d))
+    LSE = np.full((B, Hq), -np.inf)
+    for b in range(B):
+        n = int(seq_lens[b])
+        if n <= 0:
+            continue
+        t = np.arange(n)
+        pages = np.asarray(block_table[b])[t // page_size]
+        kc = k_pages[pages, t % page_size]                      # [n, Hkv, d]
+        vc = v_pages[pages, t % page_size]
+        o, l = decode_ref(q[b:b + 1], kc[None], vc[None], scale=scale)
+        O[b], LSE[b] = o[0], l[0]
+    return O, LSE

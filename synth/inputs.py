@@ -28,7 +28,7 @@ from dataclasses import dataclass
 import numpy as np
 
 ROWS_PER_BLOCK = 1024
-TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_STRESS = 0, 1, 2, 3
+TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_STRESS, TENSOR_PAGES = 0, 1, 2, 3, 4
 
 
 @dataclass(frozen=True)
@@ -160,3 +160,84 @@ def make_workload(w: Workload):
     if w.decode:
         q = q.reshape(w.B, w.Hq, w.d)
     return q, k, v
+
+
+@dataclass(frozen=True)
+class PagedWorkload:
+    """A decode step over a paged KV cache: variable lengths, shuffled pages."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    d: int
+    page_size: int
+    max_len: int          # longest sequence (max_blocks = max_len / page_size)
+    min_len: int          # shortest sequence
+    seed: int
+    spare_pages: int = 64  # pages that belong to no sequence (filled with data too)
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / np.sqrt(self.d)))
+
+    def describe(self) -> dict:
+        return {"workload": self.name, "B": self.B, "Hq": self.Hq, "Hkv": self.Hkv, "d": self.d,
+                "page_size": self.page_size, "seq_len_range": [self.min_len, self.max_len],
+                "dtype_io": "bf16", "layout": "pages [P, page, Hkv, d], block table [B, max_blocks]"}
+
+
+PAGED_WORKLOADS = {
+    "paged": PagedWorkload("paged split-KV decode B64 Hq32 Hkv8 d128 page16, lengths 4096..16384",
+                           64, 32, 8, 128, 16, 16384, 4096, 1006),
+}
+
+
+def paged_layout(B: int, page_size: int, seq_lens: np.ndarray, max_blocks: int, seed: int,
+                 spare_pages: int = 0):
+    """Block table [B, max_blocks] int32 and the page count for the given lengths.
+
+    Sequence b uses ceil(seq_lens[b] / page_size) pages. All used pages plus
+    ``spare_pages`` unused ones are numbered, shuffled with
+    ``default_rng(SeedSequence(seed, spawn_key=(4,)))`` and dealt out in sequence
+    order; unused table slots point at page 0.
+    """
+    need = [(int(n) + page_size - 1) // page_size for n in seq_lens]
+    total = sum(need) + spare_pages
+    rng = np.random.default_rng(np.random.SeedSequence(seed, spawn_key=(TENSOR_PAGES,)))
+    perm = rng.permutation(total).astype(np.int32)
+    table = np.zeros((B, max_blocks), dtype=np.int32)
+    pos = 0
+    for b in range(B):
+        table[b, :need[b]] = perm[pos:pos + need[b]]
+        pos += need[b]
+    return table, total
+
+
+def make_paged_decode(B: int, Hq: int, Hkv: int, d: int, page_size: int, seq_lens, seed: int,
+                      spare_pages: int = 0, max_blocks: int | None = None):
+    """q [B,Hq,d], k_pages/v_pages [P,page,Hkv,d] (bf16 bits), block table, seq_lens.
+
+    The page pools are i.i.d. N(0,1) rounded to bf16 (pages drawn like token rows
+    of a [1, P*page, Hkv, d] tensor); q likewise.
+    """
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    mb = max_blocks if max_blocks is not None else max(1, int(max((int(n) + page_size - 1) // page_size
+                                                                for n in seq_lens)))
+    table, P = paged_layout(B, page_size, seq_lens, mb, seed, spare_pages)
+    with ThreadPoolExecutor(_threads()) as pool:
+        q = normal_bf16((B, 1, Hq, d), seed, TENSOR_Q, pool).reshape(B, Hq, d)
+        k = normal_bf16((1, P * page_size, Hkv, d), seed, TENSOR_K, pool).reshape(P, page_size, Hkv, d)
+        v = normal_bf16((1, P * page_size, Hkv, d), seed, TENSOR_V, pool).reshape(P, page_size, Hkv, d)
+    return q, k, v, table, seq_lens
+
+
+def paged_seq_lens(w: PagedWorkload) -> np.ndarray:
+    """Lengths of a paged workload: uniform integers in [min_len, max_len]."""
+    rng = np.random.default_rng(np.random.SeedSequence(w.seed, spawn_key=(TENSOR_PAGES, 1)))
+    return rng.integers(w.min_len, w.max_len + 1, size=w.B).astype(np.int32)
+
+
+def make_paged_workload(w: PagedWorkload):
+    lens = paged_seq_lens(w)
+    return make_paged_decode(w.B, w.Hq, w.Hkv, w.d, w.page_size, lens, w.seed, w.spare_pages,
+                             max_blocks=w.max_len // w.page_size)
