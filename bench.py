@@ -99,6 +99,50 @@ def cpu_baseline(w, q, k, v, budget_s: float) -> dict:
                       f"({heads * w.Sq} query rows, all visible keys), fp64 NumPy oracle, {dt:.1f} s"}
 
 
+def paged_decode_bench(fa, dev, stream, steps: int, warmup: int) -> dict:
+    """Paged-cache split-KV decode, timed on its own after the main step.
+
+    GB/s counts the K and V bytes of every sequence's own tokens read once, plus q read
+    and O + LSE written; the block table and the split workspace are not counted.
+    """
+    import numpy as np
+    import torch
+    from synth import PAGED_WORKLOADS, make_paged_workload
+
+    w = PAGED_WORKLOADS["paged"]
+    print(f"[bench] generating inputs: {w.name}", file=sys.stderr, flush=True)
+    q, kp, vp, table, lens = make_paged_workload(w)
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    tq, tk, tv = up(q), up(kp), up(vp)
+    del kp, vp
+    tbt = torch.from_numpy(table).to(dev)
+    tsl = torch.from_numpy(lens).to(dev)
+    from io_aware_exact_21_amd.api import decode_paged_default_splits
+    ns = decode_paged_default_splits(w.B, w.Hkv, w.max_len, w.d)
+    ws = torch.empty(fa.decode_workspace_bytes(w.B, w.Hq, w.d, ns), dtype=torch.uint8, device=dev)
+    o = torch.empty((w.B, w.Hq, w.d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device=dev)
+    for _ in range(warmup):
+        fa.decode_paged(tq, tk, tv, tbt, tsl, scale=w.scale, num_splits=ns, workspace=ws, out=o, lse=lse)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fa.decode_paged(tq, tk, tv, tbt, tsl, scale=w.scale, num_splits=ns, workspace=ws, out=o, lse=lse)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = int(lens.astype(np.int64).sum()) * w.Hkv * w.d * 2 * 2 + 2 * w.B * w.Hq * w.d * 2 + w.B * w.Hq * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"config": {**w.describe(), "num_splits": ns, "seed": w.seed, "mean_len": float(lens.mean())},
+            "value": round(gbs, 1), "unit": "GB/s", "ms": round(ms, 4), "algorithmic_bytes": nbytes,
+            "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "note": "fa_decode_paged (partials + merge) timed with HIP events around the whole call"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -108,6 +152,7 @@ def main() -> int:
     ap.add_argument("--num-splits", type=int, default=0, help="decode splits (0 = library heuristic)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle CPU time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-paged", action="store_true", help="skip the paged-cache decode measurement")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run plain device copies of MIB MiB (reference reading for the HBM byte counters)")
     args = ap.parse_args()
@@ -224,6 +269,9 @@ def main() -> int:
         "wall_s_timed": round(t_wall, 3),
         "kernel_source_hash": {f: kernel_source_hash(f) for f in KERNEL_SOURCES},
     }
+    if not args.no_paged:
+        rec["paged_decode"] = paged_decode_bench(fa, dev, stream, args.steps, args.warmup)
+
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(wf, qf, kf, vf, args.cpu_budget)

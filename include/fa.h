@@ -139,6 +139,36 @@ int fa_decode_partials(const void* q, const void* k_cache, const void* v_cache,
 int fa_decode_combine(const float* part_o, const float* part_lse, void* o, float* lse,
                       int B, int Hq, int d, int num_splits, void* stream);
 
+/*
+ * fa_decode_paged - one decode step over a paged KV cache (the paged KV layout
+ * that "I/O-Aware Kernels", section FlashAttention, mentions for FlashInfer's
+ * kernels; the layout below is this library's own).
+ *
+ *   q           : bf16 [B, Hq, d]
+ *   k_pages, v_pages : bf16 [num_pages, page_size, Hkv, d]  (page pools)
+ *   block_table : int32 [B, max_blocks_per_seq]; sequence b's token t lives in
+ *                 page block_table[b, t / page_size], slot t % page_size
+ *   seq_lens    : int32 [B]; sequence b holds seq_lens[b] tokens, all visible
+ *   o, lse      : bf16 [B, Hq, d] and fp32 [B, Hq] (lse may be NULL)
+ *   page_size is a power of two in [16, 2^20]; Hq / Hkv <= 32.
+ * Chunks are cut as in fa_decode with Skv = max_blocks_per_seq * page_size
+ * (the same chunk length for every sequence); a sequence's chunks past its own
+ * length are empty. The merge is fa_decode's. num_splits <= 0 selects the larger
+ * of fa_decode_default_splits(B, Hkv, max_blocks_per_seq * page_size, d) and
+ * ceil(max_blocks_per_seq * page_size / 2048) (at most 64). The workspace is
+ * fa_decode's: fa_decode_workspace_bytes(B, Hq, d, num_splits) bytes, 256-byte
+ * aligned; to size it for the default count, pass the count computed above.
+ * block_table and seq_lens are device memory and are not read by the host:
+ * lengths are clamped to [0, max_blocks_per_seq * page_size] and page ids to
+ * [0, num_pages - 1], so bad entries give unspecified results for that
+ * sequence but never an out-of-bounds access. A sequence of length 0 gets
+ * O = 0 and LSE = -inf. block_table and seq_lens must be 4-byte aligned.
+ */
+int fa_decode_paged(const void* q, const void* k_pages, const void* v_pages, const int* block_table,
+                    const int* seq_lens, void* o, float* lse, int B, int Hq, int Hkv, int d, int page_size,
+                    int max_blocks_per_seq, int num_pages, float scale, int num_splits, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

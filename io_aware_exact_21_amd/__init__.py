@@ -6,10 +6,10 @@ pointers and the current HIP stream, and raises on any library error. Importing
 it loads libfa.so and fails loudly if the library is not built.
 """
 from . import _lib
-from .api import (decode, decode_chunk_bounds, decode_combine, decode_default_splits, decode_partials,
-                  decode_workspace_bytes, fwd)
+from .api import (decode, decode_chunk_bounds, decode_combine, decode_default_splits, decode_paged,
+                  decode_partials, decode_workspace_bytes, fwd)
 
 _lib.load()
 
-__all__ = ["fwd", "decode", "decode_partials", "decode_combine", "decode_default_splits",
+__all__ = ["fwd", "decode", "decode_paged", "decode_partials", "decode_combine", "decode_default_splits",
            "decode_workspace_bytes", "decode_chunk_bounds"]

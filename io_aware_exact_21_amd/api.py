@@ -137,3 +137,46 @@ def decode_combine(part_o: torch.Tensor, part_lse: torch.Tensor):
                                        B, Hq, d, n, _stream_ptr(part_o))
     _lib.check(st, "fa_decode_combine")
     return out, lse
+
+
+def decode_paged_default_splits(B: int, Hkv: int, max_len: int, d: int) -> int:
+    """Split count fa_decode_paged uses when num_splits <= 0 (see include/fa.h)."""
+    ns = decode_default_splits(B, Hkv, max_len, d)
+    return max(ns, min(64, (max_len + 2047) // 2048))
+
+
+def decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, block_table: torch.Tensor,
+                 seq_lens: torch.Tensor, scale=None, num_splits: int = 0, workspace: torch.Tensor | None = None,
+                 out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """Split-KV decode over a paged cache (see fa_decode_paged in include/fa.h).
+
+    q [B,Hq,d] bf16; k_pages, v_pages [num_pages, page_size, Hkv, d] bf16; block_table
+    [B, max_blocks] int32; seq_lens [B] int32 -> (o [B,Hq,d] bf16, lse [B,Hq] fp32).
+    """
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_pages, "k_pages", torch.bfloat16, 4)
+    _need(v_pages, "v_pages", torch.bfloat16, 4)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    B, Hq, d = q.shape
+    num_pages, page_size, Hkv = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    if tuple(k_pages.shape) != (num_pages, page_size, Hkv, d) or tuple(v_pages.shape) != tuple(k_pages.shape):
+        raise ValueError("k_pages/v_pages shape does not match q")
+    if block_table.shape[0] != B or tuple(seq_lens.shape) != (B,):
+        raise ValueError("block_table / seq_lens must have one row per sequence")
+    max_blocks = block_table.shape[1]
+    ns = num_splits if num_splits > 0 else decode_paged_default_splits(B, Hkv, max_blocks * page_size, d)
+    if workspace is None:
+        workspace = torch.empty(decode_workspace_bytes(B, Hq, d, ns), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.bfloat16, 3)
+    _need(lse, "lse", torch.float32, 2)
+    st = _lib.load().fa_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), block_table.data_ptr(),
+                                     seq_lens.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, d, page_size,
+                                     max_blocks, num_pages, _scale(scale, d), ns, workspace.data_ptr(),
+                                     workspace.numel() * workspace.element_size(), _stream_ptr(q))
+    _lib.check(st, "fa_decode_paged")
+    return out, lse

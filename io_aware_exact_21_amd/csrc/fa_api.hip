@@ -110,6 +110,37 @@ int partials_impl(const void* q, const void* k, const void* v, float* part_o, fl
   return FA_OK;
 }
 
+int paged_partials_impl(const void* q, const void* k_pages, const void* v_pages, const int* block_table,
+                        const int* seq_lens, float* part_o, float* part_lse, int B, int Hq, int Hkv, int d,
+                        int page_log2, int max_blocks, int num_pages, float scale, int nsplit, hipStream_t stream) {
+  fa::DecParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k_pages);
+  p.v = static_cast<const uint16_t*>(v_pages);
+  p.part_o = part_o;
+  p.part_lse = part_lse;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.d = d;
+  p.Skv = max_blocks << page_log2;
+  p.nsplit = nsplit;
+  p.chunk = split_chunk(p.Skv, nsplit);
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.page_log2 = page_log2;
+  p.max_blocks = max_blocks;
+  p.num_pages = num_pages;
+  int st = scale_terms(scale, &p.c, &p.qsign, &p.qmask);
+  if (st != FA_OK) return st;
+  (void)hipGetLastError();
+  if (fa::launch_decode_paged_partials(p, stream) != hipSuccess) return FA_ERR_HIP;
+  return FA_OK;
+}
+
+int log2_exact(int x) {
+  int l = 0;
+  while ((1 << l) < x && l < 30) ++l;
+  return (1 << l) == x ? l : -1;
+}
+
 }  // namespace
 
 extern "C" {
@@ -194,6 +225,45 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, 
                                              align256((size_t)B * Hq * num_splits * d * sizeof(float)));
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = partials_impl(q, k_cache, v_cache, part_o, part_lse, B, Hq, Hkv, Skv, d, scale, num_splits, s);
+  if (st != FA_OK) return st;
+  return combine_impl(part_o, part_lse, o, lse, B, Hq, d, num_splits, s);
+}
+
+int fa_decode_paged(const void* q, const void* k_pages, const void* v_pages, const int* block_table,
+                    const int* seq_lens, void* o, float* lse, int B, int Hq, int Hkv, int d, int page_size,
+                    int max_blocks_per_seq, int num_pages, float scale, int num_splits, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (!q || !k_pages || !v_pages || !block_table || !seq_lens || !o) return FA_ERR_NULL;
+  if (B < 1 || Hq < 1 || Hkv < 1 || max_blocks_per_seq < 1 || num_pages < 1) return FA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (Hq / Hkv > 32) return FA_ERR_UNSUPPORTED;
+  const int page_log2 = log2_exact(page_size);
+  if (page_log2 < 4 || page_log2 > 20) return FA_ERR_SHAPE;     // power of two, 16 .. 2^20 tokens
+  const double max_len = (double)max_blocks_per_seq * page_size;
+  if (max_len > 2.0e9 || (double)num_pages * page_size * Hkv * d > 4.0e18 || (double)B * max_blocks_per_seq > 2.0e9 ||
+      (double)B * Hq > 2.0e9)
+    return FA_ERR_SHAPE;
+  if (num_splits <= 0) {
+    // lengths vary per sequence: besides filling the CUs, keep chunks near 2048 keys so
+    // that long and short sequences spread over many equal workgroups
+    num_splits = fa_decode_default_splits(B, Hkv, (int)max_len, d);
+    const long long by_len = ((long long)max_len + 2047) / 2048;
+    if (by_len > num_splits) num_splits = (int)(by_len < 64 ? by_len : 64);
+  }
+  if (num_splits < 1 || (double)B * Hkv * num_splits > 2.0e9) return FA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o) || (lse && !aligned16(lse)) ||
+      (reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
+    return FA_ERR_ALIGN;
+  const size_t need = fa_decode_workspace_bytes(B, Hq, d, num_splits);
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || workspace_bytes < need)
+    return FA_ERR_WORKSPACE;
+  float* part_o = static_cast<float*>(workspace);
+  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                             align256((size_t)B * Hq * num_splits * d * sizeof(float)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int st = paged_partials_impl(q, k_pages, v_pages, block_table, seq_lens, part_o, part_lse, B, Hq, Hkv, d,
+                               page_log2, max_blocks_per_seq, num_pages, scale, num_splits, s);
   if (st != FA_OK) return st;
   return combine_impl(part_o, part_lse, o, lse, B, Hq, d, num_splits, s);
 }

@@ -16,21 +16,95 @@
 
 namespace fa {
 
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void fa_decode_split_kernel(DecParams p) {
+// Copy of one K tile and one V tile of a paged cache (global -> registers -> LDS).
+// Thread t copies 16-byte column t % CPR of PER_T consecutive keys, starting at key
+// (t / CPR) * PER_T of the tile. Those keys share one page (pages hold at least 16
+// tokens and PER_T <= 8 divides 16), so a thread needs a single page-table entry per
+// tile, looked up one tile ahead by fetch_page.
+template <int D, int BCT, int NT>
+struct PagedTileCopy : TileCopy<D, BCT, NT> {
+  using Base = TileCopy<D, BCT, NT>;
+  using Base::CPR;
+  using Base::PER_T;
+  static_assert(Base::CHUNKS == PER_T * NT && NT % CPR == 0, "every thread copies PER_T whole chunks");
+  static_assert(PER_T <= 16 && 16 % PER_T == 0, "a thread's keys must stay inside one 16-token page");
+
+  __device__ __forceinline__ static int first_key(int tid) { return (tid / CPR) * PER_T; }
+
+  // Page id of this thread's keys in the tile starting at key k0 (0 when they are all
+  // at or past kmax). Ids outside [0, num_pages) are clamped, so a bad table entry
+  // cannot read outside the page pool.
+  __device__ __forceinline__ static int fetch_page(const int* __restrict__ bt_row, int k0, int kmax,
+                                                   int page_log2, int num_pages, int tid) {
+    const int key = k0 + first_key(tid);
+    return key < kmax ? min(max(bt_row[key >> page_log2], 0), num_pages - 1) : 0;
+  }
+
+  // kp / vp: page pool base + this head's offset; row_stride = Hkv * D elements.
+  __device__ __forceinline__ void load_paged(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
+                                             int64_t row_stride, int page_log2, int k0, int kmax, int pid,
+                                             int tid) {
+    const int pmask = (1 << page_log2) - 1;
+    const int key0 = k0 + first_key(tid), c = tid % CPR;
+    const int64_t base = (((int64_t)pid << page_log2) + (key0 & pmask)) * row_stride + c * 8;
+#pragma unroll
+    for (int p = 0; p < PER_T; ++p) {
+      u32x4 zk = {0u, 0u, 0u, 0u}, zv = {0u, 0u, 0u, 0u};
+      if (key0 + p < kmax) {
+        zk = *reinterpret_cast<const u32x4*>(kp + base + p * row_stride);
+        zv = *reinterpret_cast<const u32x4*>(vp + base + p * row_stride);
+      }
+      this->kr[p] = zk;
+      this->vr[p] = zv;
+    }
+  }
+
+  __device__ __forceinline__ void store_paged(uint16_t* ks, uint16_t* vs, int tid) const {
+    const int key0 = first_key(tid), c = tid % CPR;
+#pragma unroll
+    for (int p = 0; p < PER_T; ++p) {
+      const int key = key0 + p;
+      *reinterpret_cast<u32x4*>(ks + key * D + ((c ^ k_swz<D>(key)) << 3)) = this->kr[p];
+      *reinterpret_cast<u32x4*>(vs + key * D + ((c ^ v_swz<D>(key)) << 3)) = this->vr[p];
+    }
+  }
+};
+
+// Register budget: two waves per SIMD (<= 256 VGPRs), so four workgroups share a CU
+// and each keeps its next tile in flight in registers while the current one sits in
+// its single LDS buffer: twice the bytes in flight per CU of one wave per SIMD.
+template <int D, int NW, bool PAGED>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void fa_decode_split_kernel(DecParams p) {
   constexpr int BCT = 32 * NW;
   constexpr int NT = NW * 64;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2][2][BCT * D];
-  static_assert(sizeof(smem) >= NW * 32 * (D + 2) * sizeof(float), "merge buffer must fit");
+  using Copy = PagedTileCopy<D, BCT, NT>;
+  // One LDS buffer for the current K and V tiles, reused for the final merge of the
+  // waves' partial results.
+  constexpr int KV_BYTES = 2 * BCT * D * 2;
+  constexpr int MERGE_BYTES = NW * 32 * (D + 2) * 4;
+  __shared__ __attribute__((aligned(16))) uint16_t smem_raw[(KV_BYTES > MERGE_BYTES ? KV_BYTES : MERGE_BYTES) / 2];
+  uint16_t* const ksm = smem_raw;
+  uint16_t* const vsm = smem_raw + BCT * D;
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
-  const int cidx = blockIdx.x % p.nsplit;
-  const int bh = blockIdx.x / p.nsplit;
+  // Chunk-major order: every (sequence, head) takes its first chunk before any takes
+  // its second. Workgroups are dealt round-robin to the XCDs, so this hands each XCD the
+  // same mix of chunk indices; with variable lengths the empty chunks (high indices of
+  // short sequences) come last instead of all landing on the XCDs of those indices.
+  const int units = p.B * p.Hkv;
+  const int cidx = blockIdx.x / units;
+  const int bh = blockIdx.x - cidx * units;
   const int b = bh / p.Hkv, hk = bh - b * p.Hkv;
   const int grp = p.Hq / p.Hkv;                       // query heads per KV head (<= 32)
+  // Keys of this sequence and this chunk. Chunks have one length for every sequence
+  // (cut from the longest possible one), so workgroups carry equal work whatever the
+  // mix of lengths; a paged sequence holds seq_lens[b] tokens (clamped to its table)
+  // and its chunks past that length are empty.
+  int skv = p.Skv;
+  if (PAGED) skv = min(max(p.seq_lens[b], 0), p.max_blocks << p.page_log2);
   const int c0 = cidx * p.chunk;
-  const int c1 = min(p.Skv, c0 + p.chunk);
+  const int c1 = min(skv, c0 + p.chunk);
   const int nk = c1 > c0 ? c1 - c0 : 0;
   const int ntiles = (nk + BCT - 1) / BCT;
 
@@ -50,8 +124,10 @@ __global__ __launch_bounds__(NW * 64) void fa_decode_split_kernel(DecParams p) {
   }
 
   const int64_t kv_stride = (int64_t)p.Hkv * D;
-  const uint16_t* kb = p.k + ((int64_t)b * p.Skv * p.Hkv + hk) * D;
-  const uint16_t* vb = p.v + ((int64_t)b * p.Skv * p.Hkv + hk) * D;
+  // contiguous: this sequence's rows; paged: the page pool, offset to this KV head
+  const uint16_t* kb = PAGED ? p.k + (int64_t)hk * D : p.k + ((int64_t)b * p.Skv * p.Hkv + hk) * D;
+  const uint16_t* vb = PAGED ? p.v + (int64_t)hk * D : p.v + ((int64_t)b * p.Skv * p.Hkv + hk) * D;
+  const int* bt_row = PAGED ? p.block_table + (int64_t)b * p.max_blocks : nullptr;
 
   f32x16 O[D / 32];
 #pragma unroll
@@ -59,19 +135,35 @@ __global__ __launch_bounds__(NW * 64) void fa_decode_split_kernel(DecParams p) {
   float m_run = -INFINITY, l_run = 0.f;
   const float c = p.c;
 
-  TileCopy<D, BCT, NT> cp;
+  Copy cp;
+  int pid = 0;               // paged: page of this thread's keys in the next tile to copy
   if (ntiles > 0) {
-    cp.load(kb, vb, kv_stride, c0, c1, tid);
-    cp.store(smem[0][0], smem[0][1], tid);
+    if (PAGED) {
+      pid = Copy::fetch_page(bt_row, c0, c1, p.page_log2, p.num_pages, tid);
+      cp.load_paged(kb, vb, kv_stride, p.page_log2, c0, c1, pid, tid);
+      pid = Copy::fetch_page(bt_row, c0 + BCT, c1, p.page_log2, p.num_pages, tid);
+      cp.store_paged(ksm, vsm, tid);
+    } else {
+      cp.load(kb, vb, kv_stride, c0, c1, tid);
+      cp.store(ksm, vsm, tid);
+    }
   }
   __syncthreads();
 
   for (int j = 0; j < ntiles; ++j) {
     const int k0 = c0 + j * BCT;
     const bool more = j + 1 < ntiles;
-    if (more) cp.load(kb, vb, kv_stride, k0 + BCT, c1, tid);
-    const uint16_t* ks = smem[j & 1][0];
-    const uint16_t* vs = smem[j & 1][1];
+    if (more) {
+      if (PAGED) {
+        cp.load_paged(kb, vb, kv_stride, p.page_log2, k0 + BCT, c1, pid, tid);
+        // page of the tile after next, one tile ahead of its use
+        pid = Copy::fetch_page(bt_row, k0 + 2 * BCT, c1, p.page_log2, p.num_pages, tid);
+      } else {
+        cp.load(kb, vb, kv_stride, k0 + BCT, c1, tid);
+      }
+    }
+    const uint16_t* ks = ksm;
+    const uint16_t* vs = vsm;
 
     const int kw = k0 + 32 * w;
     if (kw < c1) {
@@ -109,12 +201,16 @@ __global__ __launch_bounds__(NW * 64) void fa_decode_split_kernel(DecParams p) {
       pv_step<D>(vs, g, 2 * w + 1, p_operand(S, 1), O);
     }
 
-    if (more) cp.store(smem[(j + 1) & 1][0], smem[(j + 1) & 1][1], tid);
+    __syncthreads();    // every wave is done with tile j in LDS
+    if (more) {
+      if (PAGED) cp.store_paged(ksm, vsm, tid);
+      else cp.store(ksm, vsm, tid);
+    }
     __syncthreads();
   }
 
   // ---- merge the NW waves' partial results through LDS ------------------------------
-  float* mrow = reinterpret_cast<float*>(&smem[0][0][0]);   // [NW][32]
+  float* mrow = reinterpret_cast<float*>(smem_raw);         // [NW][32]
   float* lrow = mrow + NW * 32;                              // [NW][32]
   float* obuf = lrow + NW * 32;                              // [NW][32][D]
   const float l_tot = pair_sum(l_run);
@@ -183,16 +279,20 @@ __global__ __launch_bounds__(256) void fa_decode_combine_kernel(CombineParams p)
   if (p.lse != nullptr && lane == 0) p.lse[row] = W > 0.f ? M + fast_log2(W) * kLn2 : -INFINITY;
 }
 
-hipError_t launch_decode_partials(const DecParams& p, hipStream_t stream) {
+template <bool PAGED>
+static hipError_t launch_split(const DecParams& p, hipStream_t stream) {
   const long long grid = (long long)p.B * p.Hkv * p.nsplit;
   if (p.d == 128)
-    hipLaunchKernelGGL((fa_decode_split_kernel<128, kDecWaves>), dim3((unsigned)grid), dim3(kDecWaves * 64), 0,
-                       stream, p);
+    hipLaunchKernelGGL((fa_decode_split_kernel<128, kDecWaves, PAGED>), dim3((unsigned)grid), dim3(kDecWaves * 64),
+                       0, stream, p);
   else
-    hipLaunchKernelGGL((fa_decode_split_kernel<64, kDecWaves>), dim3((unsigned)grid), dim3(kDecWaves * 64), 0,
-                       stream, p);
+    hipLaunchKernelGGL((fa_decode_split_kernel<64, kDecWaves, PAGED>), dim3((unsigned)grid), dim3(kDecWaves * 64),
+                       0, stream, p);
   return hipGetLastError();
 }
+
+hipError_t launch_decode_partials(const DecParams& p, hipStream_t stream) { return launch_split<false>(p, stream); }
+hipError_t launch_decode_paged_partials(const DecParams& p, hipStream_t stream) { return launch_split<true>(p, stream); }
 
 hipError_t launch_decode_combine(const CombineParams& p, hipStream_t stream) {
   const unsigned grid = (unsigned)((p.rows + 3) / 4);

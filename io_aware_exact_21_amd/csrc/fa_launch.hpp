@@ -32,10 +32,16 @@ struct DecParams {
   float* part_o;    // [B, Hq, nsplit, d]
   float* part_lse;  // [B, Hq, nsplit]
   int B, Hq, Hkv, Skv, d;
-  int nsplit, chunk;  // chunk = keys per split (multiple of kSplitAlign)
+  int nsplit, chunk;  // chunk = keys per split (multiple of kSplitAlign); contiguous caches only
   float c;
   unsigned qsign;
   unsigned qmask;
+  // Paged caches only: k and v are page pools [num_pages, page_size, Hkv, d];
+  // sequence b's token t lives in page block_table[b * max_blocks + t / page_size]
+  // at slot t % page_size, and the sequence holds seq_lens[b] tokens.
+  const int* block_table;   // [B, max_blocks]
+  const int* seq_lens;      // [B]
+  int page_log2, max_blocks, num_pages;
 };
 
 struct CombineParams {
@@ -50,6 +56,7 @@ struct CombineParams {
 long long fwd_grid_size(int B, int Hq, int Sq);
 hipError_t launch_fwd(const FwdParams& p, bool causal, bool out_f32, hipStream_t stream);
 hipError_t launch_decode_partials(const DecParams& p, hipStream_t stream);
+hipError_t launch_decode_paged_partials(const DecParams& p, hipStream_t stream);
 hipError_t launch_decode_combine(const CombineParams& p, hipStream_t stream);
 
 }  // namespace fa

@@ -25,7 +25,7 @@ def declared_functions():
 def test_header_declares_expected_entry_points():
     names = declared_functions()
     for n in ("fa_fwd", "fa_decode", "fa_decode_combine", "fa_decode_partials", "fa_decode_workspace_bytes",
-              "fa_decode_default_splits", "fa_status_string", "fa_fwd_f32out"):
+              "fa_decode_default_splits", "fa_status_string", "fa_fwd_f32out", "fa_decode_paged"):
         assert n in names
 
 
@@ -118,3 +118,30 @@ def test_binding_rejects_cpu_tensors():
     q = torch.zeros(1, 4, 1, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="no CPU path"):
         fa.fwd(q, q, q)
+
+
+def test_paged_decode_validation(lib):
+    from io_aware_exact_21_amd._lib import (FA_ERR_ALIGN, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED,
+                                            FA_ERR_WORKSPACE)
+    need = lib.fa_decode_workspace_bytes(2, 8, 128, 4)
+
+    def dec(q=A, kp=A, bt=A, sl=A, o=A, ws=A, wsb=None, Hq=8, Hkv=2, d=128, ps=16, mb=8, npg=32, ns=4):
+        return lib.fa_decode_paged(q, kp, A, bt, sl, o, None, 2, Hq, Hkv, d, ps, mb, npg, 0.1, ns, ws,
+                                   need if wsb is None else wsb, None)
+    assert dec(q=None) == FA_ERR_NULL
+    assert dec(kp=None) == FA_ERR_NULL
+    assert dec(bt=None) == FA_ERR_NULL
+    assert dec(sl=None) == FA_ERR_NULL
+    assert dec(o=None) == FA_ERR_NULL
+    assert dec(ps=24) == FA_ERR_SHAPE                  # not a power of two
+    assert dec(ps=8) == FA_ERR_SHAPE                   # below 16 tokens
+    assert dec(ps=0) == FA_ERR_SHAPE
+    assert dec(mb=0) == FA_ERR_SHAPE
+    assert dec(npg=0) == FA_ERR_SHAPE
+    assert dec(Hq=7) == FA_ERR_SHAPE
+    assert dec(Hq=66, Hkv=2) == FA_ERR_UNSUPPORTED
+    assert dec(d=96) == FA_ERR_UNSUPPORTED
+    assert dec(ws=None) == FA_ERR_WORKSPACE
+    assert dec(wsb=need - 1) == FA_ERR_WORKSPACE
+    assert dec(bt=A + 2) == FA_ERR_ALIGN
+    assert dec(q=A + 8) == FA_ERR_ALIGN
