@@ -139,7 +139,10 @@ def paged_decode_bench(fa, dev, stream, steps: int, warmup: int) -> dict:
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"config": {**w.describe(), "num_splits": ns, "seed": w.seed, "mean_len": float(lens.mean())},
             "value": round(gbs, 1), "unit": "GB/s", "ms": round(ms, 4), "algorithmic_bytes": nbytes,
-            "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": measured_traffic("fa_decode_paged_hbm_traffic.txt", "decode"),
+                         "kernel": "fa_decode_split_kernel (paged) + fa_decode_combine_kernel"},
             "note": "fa_decode_paged (partials + merge) timed with HIP events around the whole call"}
 
 
