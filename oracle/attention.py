@@ -1,4 +1,4 @@
-"""Plain fp64 CPU oracle for exact attention, its streamed form and the split-KV merge.
+"""Plain fp64 CPU oracle for exact attention, its gradients, its streamed form and the split-KV merge.
 
 TEST INFRASTRUCTURE ONLY. This module is the yardstick the GPU library is
 checked against. Only the tests, the smoke check and the benchmark's CPU
@@ -240,3 +240,70 @@ def paged_decode_ref(q: np.ndarray, k_pages: np.ndarray, v_pages: np.ndarray, bl
         o, l = decode_ref(q[b:b + 1], kc[None], vc[None], scale=scale)
         O[b], LSE[b] = o[0], l[0]
     return O, LSE
+
+
+def attention_bwd_rows(q_rows: np.ndarray, do_rows: np.ndarray, K: np.ndarray, V: np.ndarray,
+                       rows: np.ndarray, Sq: int, causal: bool, scale: float):
+    """Gradients from selected query rows of one (batch, query head).
+
+    [GRASP, Conclusion] says the backward pass recomputes the attention matrix
+    instead of storing it. The pages give no formulas, so this is the derivative of
+    the forward definition above by the chain rule, with the probabilities rebuilt
+    from Q and K (nothing from the forward is reused). For loss gradient dO:
+
+        P_ij   = softmax_j(s_ij) over j in A(i),  s_ij = scale * Q_i . K_j
+        dV_j  += sum_i P_ij dO_i
+        dP_ij  = dO_i . V_j
+        dS_ij  = P_ij (dP_ij - sum_k P_ik dP_ik)     (gradient of the scaled score)
+        dQ_i   = scale * sum_j dS_ij K_j
+        dK_j  += scale * sum_i dS_ij Q_i
+
+    q_rows, do_rows [n, d] are rows ``rows`` of that head; K, V [Skv, d] its KV head.
+    Returns dQ [n, d] and this block's contributions dK, dV [Skv, d] (float64). A row
+    with no visible key contributes nothing and gets dQ = 0.
+    """
+    rows = np.asarray(rows)
+    Skv = K.shape[0]
+    sigma = _sigma(scale)
+    s = sigma * (q_rows @ K.T)                                   # [n, Skv]
+    nvis = np.array([visible_keys(int(i), Sq, Skv, causal) for i in rows])
+    keep = np.arange(Skv)[None, :] < nvis[:, None]
+    P = np.zeros_like(s)
+    live = nvis > 0
+    if live.any():
+        sl = np.where(keep[live], s[live], -np.inf)
+        w = np.exp(sl - sl.max(axis=1, keepdims=True))
+        P[live] = w / w.sum(axis=1, keepdims=True)
+    dP = do_rows @ V.T                                           # [n, Skv]
+    dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+    return sigma * (dS @ K), sigma * (dS.T @ q_rows), P.T @ do_rows
+
+
+def attention_bwd_ref(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, *, causal: bool,
+                      scale: float, row_block: int = 512):
+    """Gradients of exact attention with respect to Q, K and V.
+
+    q, do [B,Sq,Hq,d]; k, v [B,Skv,Hkv,d]; all float64. The loss gradient dO is the
+    gradient with respect to the output O of ``attention_ref``. A KV head's gradients
+    sum the contributions of every query head that reads it.
+    Returns dQ [B,Sq,Hq,d], dK and dV [B,Skv,Hkv,d] (float64).
+    """
+    B, Sq, Hq, d = q.shape
+    Bk, Skv, Hkv, dk = k.shape
+    if Bk != B or dk != d or v.shape != k.shape or do.shape != q.shape or Hq % Hkv != 0:
+        raise ValueError("inconsistent shapes")
+    dQ = np.zeros((B, Sq, Hq, d))
+    dK = np.zeros((B, Skv, Hkv, d))
+    dV = np.zeros((B, Skv, Hkv, d))
+    for b in range(B):
+        for h in range(Hq):
+            hk = kv_head_of(h, Hq, Hkv)
+            K, V = k[b, :, hk, :], v[b, :, hk, :]
+            for r0 in range(0, Sq, row_block):
+                rows = np.arange(r0, min(Sq, r0 + row_block))
+                gq, gk, gv = attention_bwd_rows(q[b, rows, h, :], do[b, rows, h, :], K, V, rows, Sq,
+                                                causal, scale)
+                dQ[b, rows, h, :] = gq
+                dK[b, :, hk, :] += gk
+                dV[b, :, hk, :] += gv
+    return dQ, dK, dV

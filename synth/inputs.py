@@ -18,6 +18,8 @@ Recipe (the pages state only "i.i.d. N(0,1) from seed"; this is the reading):
   distinct token positions per batch element (all KV heads). The positions come
   from ``default_rng(SeedSequence(seed, spawn_key=(3, b))).choice(Skv, n,
   replace=False)``. Multiplying by 4 only adds 2 to the exponent, so it is exact.
+* The loss gradient dO of a backward step is drawn like Q (same shape, same
+  recipe) with tensor id 5.
 """
 from __future__ import annotations
 
@@ -28,7 +30,7 @@ from dataclasses import dataclass
 import numpy as np
 
 ROWS_PER_BLOCK = 1024
-TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_STRESS, TENSOR_PAGES = 0, 1, 2, 3, 4
+TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_STRESS, TENSOR_PAGES, TENSOR_DO = 0, 1, 2, 3, 4, 5
 
 
 @dataclass(frozen=True)
@@ -152,6 +154,12 @@ def make_qkv(B: int, Hq: int, Hkv: int, Sq: int, Skv: int, d: int, seed: int,
             pos = stress_positions(seed, b, Skv, k_stress_frac)
             k[b, pos] = times4_bf16(k[b, pos])
     return q, k, v
+
+
+def make_grad_out(B: int, Sq: int, Hq: int, d: int, seed: int) -> np.ndarray:
+    """Loss gradient dO [B,Sq,Hq,d] for a backward step, bf16 bits (tensor id 5)."""
+    with ThreadPoolExecutor(_threads()) as pool:
+        return normal_bf16((B, Sq, Hq, d), seed, TENSOR_DO, pool)
 
 
 def make_workload(w: Workload):
