@@ -243,7 +243,7 @@ def paged_decode_ref(q: np.ndarray, k_pages: np.ndarray, v_pages: np.ndarray, bl
 
 
 def attention_bwd_rows(q_rows: np.ndarray, do_rows: np.ndarray, K: np.ndarray, V: np.ndarray,
-                       rows: np.ndarray, Sq: int, causal: bool, scale: float):
+                       rows: np.ndarray, Sq: int, causal: bool, scale: float, abs_terms: bool = False):
     """Gradients from selected query rows of one (batch, query head).
 
     [GRASP, Conclusion] says the backward pass recomputes the attention matrix
@@ -261,6 +261,22 @@ def attention_bwd_rows(q_rows: np.ndarray, do_rows: np.ndarray, K: np.ndarray, V
     q_rows, do_rows [n, d] are rows ``rows`` of that head; K, V [Skv, d] its KV head.
     Returns dQ [n, d] and this block's contributions dK, dV [Skv, d] (float64). A row
     with no visible key contributes nothing and gets dQ = 0.
+
+    With ``abs_terms`` it also returns two sensitivity measures per output element, for
+    relative perturbations of the factor dS (dQ, dK) or P (dV) of every product term
+    and of every element of the output O entering D_i = dO_i . O_i (a backward pass
+    receives O rounded to the output format). With E_i = sum_c |dO_ic| |O_ic| and
+    F_i = (sum_c dO_ic^2 O_ic^2)^(1/2):
+      * worst case (all perturbations of size 1, signs adversarial):
+          dQ: |scale| (sum_j |dS_ij| |K_j| + E_i sum_j P_ij |K_j|)
+          dK: |scale| (sum_i |dS_ij| |Q_i| + sum_i P_ij E_i |Q_i|)
+          dV: sum_i P_ij |dO_i|
+      * root-sum-square (independent perturbations of unit variance):
+          dQ: |scale| (sum_j dS_ij^2 K_j^2 + F_i^2 (sum_j P_ij K_j)^2)^(1/2)
+          dK: |scale| (sum_i dS_ij^2 Q_i^2 + sum_i P_ij^2 F_i^2 Q_i^2)^(1/2)
+          dV: (sum_i P_ij^2 dO_i^2)^(1/2)
+    (elementwise over the head dimension). In ``attention_bwd_ref`` the squared
+    root-sum-square terms add over row blocks, so this function returns them squared.
     """
     rows = np.asarray(rows)
     Skv = K.shape[0]
@@ -276,34 +292,56 @@ def attention_bwd_rows(q_rows: np.ndarray, do_rows: np.ndarray, K: np.ndarray, V
         P[live] = w / w.sum(axis=1, keepdims=True)
     dP = do_rows @ V.T                                           # [n, Skv]
     dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
-    return sigma * (dS @ K), sigma * (dS.T @ q_rows), P.T @ do_rows
+    grads = (sigma * (dS @ K), sigma * (dS.T @ q_rows), P.T @ do_rows)
+    if not abs_terms:
+        return grads
+    aS = abs(sigma) * np.abs(dS)
+    O = P @ V
+    E = (np.abs(do_rows) * np.abs(O)).sum(axis=1)                 # sum_c |dO_ic| |O_ic|
+    F2 = (do_rows ** 2 * O ** 2).sum(axis=1)                      # sum_c dO_ic^2 O_ic^2
+    aK, aQ = np.abs(K), np.abs(q_rows)
+    s2 = sigma * sigma
+    worst = (aS @ aK + abs(sigma) * E[:, None] * (P @ aK),
+             aS.T @ aQ + abs(sigma) * (P.T @ (E[:, None] * aQ)),
+             P.T @ np.abs(do_rows))
+    rss2 = (s2 * ((dS ** 2) @ (K ** 2) + F2[:, None] * (P @ K) ** 2),
+            s2 * ((dS ** 2).T @ (q_rows ** 2) + (P ** 2).T @ (F2[:, None] * q_rows ** 2)),
+            (P ** 2).T @ (do_rows ** 2))
+    return grads + worst + rss2
 
 
 def attention_bwd_ref(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, *, causal: bool,
-                      scale: float, row_block: int = 512):
+                      scale: float, row_block: int = 512, abs_terms: bool = False):
     """Gradients of exact attention with respect to Q, K and V.
 
     q, do [B,Sq,Hq,d]; k, v [B,Skv,Hkv,d]; all float64. The loss gradient dO is the
     gradient with respect to the output O of ``attention_ref``. A KV head's gradients
     sum the contributions of every query head that reads it.
-    Returns dQ [B,Sq,Hq,d], dK and dV [B,Skv,Hkv,d] (float64).
+    Returns dQ [B,Sq,Hq,d], dK and dV [B,Skv,Hkv,d] (float64); with ``abs_terms`` also
+    the worst-case and the root-sum-square sensitivities of ``attention_bwd_rows`` for
+    dQ, dK, dV, in the same shapes (nine arrays in all).
     """
     B, Sq, Hq, d = q.shape
     Bk, Skv, Hkv, dk = k.shape
     if Bk != B or dk != d or v.shape != k.shape or do.shape != q.shape or Hq % Hkv != 0:
         raise ValueError("inconsistent shapes")
-    dQ = np.zeros((B, Sq, Hq, d))
-    dK = np.zeros((B, Skv, Hkv, d))
-    dV = np.zeros((B, Skv, Hkv, d))
+    out = [np.zeros((B, Sq, Hq, d)), np.zeros((B, Skv, Hkv, d)), np.zeros((B, Skv, Hkv, d))]
+    if abs_terms:
+        for _ in range(2):
+            out += [np.zeros((B, Sq, Hq, d)), np.zeros((B, Skv, Hkv, d)), np.zeros((B, Skv, Hkv, d))]
     for b in range(B):
         for h in range(Hq):
             hk = kv_head_of(h, Hq, Hkv)
             K, V = k[b, :, hk, :], v[b, :, hk, :]
             for r0 in range(0, Sq, row_block):
                 rows = np.arange(r0, min(Sq, r0 + row_block))
-                gq, gk, gv = attention_bwd_rows(q[b, rows, h, :], do[b, rows, h, :], K, V, rows, Sq,
-                                                causal, scale)
-                dQ[b, rows, h, :] = gq
-                dK[b, :, hk, :] += gk
-                dV[b, :, hk, :] += gv
-    return dQ, dK, dV
+                res = attention_bwd_rows(q[b, rows, h, :], do[b, rows, h, :], K, V, rows, Sq, causal, scale,
+                                         abs_terms)
+                for n in range(0, len(res), 3):
+                    out[n][b, rows, h, :] = res[n]
+                    out[n + 1][b, :, hk, :] += res[n + 1]
+                    out[n + 2][b, :, hk, :] += res[n + 2]
+    if abs_terms:
+        for n in (6, 7, 8):
+            out[n] = np.sqrt(out[n])
+    return tuple(out)

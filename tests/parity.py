@@ -64,3 +64,36 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
     f, e = np.frexp(x)
     sp = np.ldexp(1.0, np.maximum(e, -125) - 8)
     return np.rint(x / sp) * sp
+
+
+GRAD_TERM = 2.0 ** -8
+
+
+def check_grad(g_gpu: np.ndarray, g_ref: np.ndarray, a_ref: np.ndarray, r_ref: np.ndarray, what: str) -> dict:
+    """Gradient check (bf16 output). The tolerance stated for O and LSE does not cover
+    gradients; this one follows from the arithmetic. Two roundings to bf16 (unit
+    roundoff u = 2^-8) enter every gradient element: one factor of each product term
+    (dS for dQ and dK, P for dV) is rounded before the fp32 MFMA accumulate, and D_i is
+    formed from the bf16 O the forward returns. a_ref and r_ref (oracle, abs_terms) are
+    the element's worst-case and root-sum-square first-order sensitivities to relative
+    changes of those factors, so the rounding error is at most u * a_ref and, for
+    independent roundings (relative error uniform in [-u, u], RMS u / sqrt(3)), has RMS
+    (u / sqrt(3)) * r_ref. fp32 arithmetic and the fp32 LSE add far less and are
+    covered by the forward's 1e-2. Per element:
+    |err| <= 1e-2 + half a bf16 spacing at the exact value + 2^-8 * a_ref.
+    Per tensor, the forward's rel-L2 bar plus twice the expected RMS of the rounding:
+    ||err||_2 <= 4e-3 ||g_ref||_2 + 2 (2^-8 / sqrt(3)) ||r_ref||_2.
+    """
+    err = np.abs(g_gpu - g_ref)
+    bound = MAX_ABS + half_spacing_bf16(g_ref) + GRAD_TERM * a_ref
+    nref = np.linalg.norm(g_ref)
+    rel = np.linalg.norm(g_gpu - g_ref) / nref if nref > 0 else np.linalg.norm(g_gpu)
+    rel_bound = REL_L2 + 2.0 * (GRAD_TERM / np.sqrt(3.0)) * (np.linalg.norm(r_ref) / nref if nref > 0 else 0.0)
+    worst = np.unravel_index(np.argmax(err - bound), err.shape) if err.size else None
+    info = {"max_abs": float(err.max()) if err.size else 0.0, "rel_l2": float(rel), "rel_l2_bound": float(rel_bound),
+            "max_err_over_bound": float((err / bound).max()) if err.size else 0.0}
+    assert np.isfinite(g_gpu).all(), f"{what}: non-finite output"
+    assert (err <= bound).all(), (f"{what}: |err| {err[worst]:.4e} > bound {bound[worst]:.4e} at {worst} "
+                                  f"(gpu {g_gpu[worst]}, ref {g_ref[worst]}, abs-terms {a_ref[worst]:.4e}); {info}")
+    assert rel <= rel_bound, f"{what}: rel-L2 {rel:.3e} > {rel_bound:.3e}; {info}"
+    return info

@@ -132,3 +132,83 @@ def test_grouped_heads_sum_over_group():
     np.testing.assert_allclose(dq, dq1, atol=1e-13)
     np.testing.assert_allclose(dk, dk1.reshape(B, Skv, Hkv, g, d).sum(axis=3), atol=1e-13)
     np.testing.assert_allclose(dv, dv1.reshape(B, Skv, Hkv, g, d).sum(axis=3), atol=1e-13)
+
+
+def test_sensitivity_sums():
+    # the sensitivity sums bound the gradients (triangle inequality), equal dV when every
+    # term has one sign (dO >= 0; dV does not depend on D), and do not change the gradients
+    q, k, v, do = _inputs(1, 30, 40, 4, 2, 8, seed=19)
+    for causal in (False, True):
+        g = attention_bwd_ref(q, k, v, do, causal=causal, scale=-0.45, row_block=11)
+        ga = attention_bwd_ref(q, k, v, do, causal=causal, scale=-0.45, row_block=11, abs_terms=True)
+        assert len(g) == 3 and len(ga) == 9
+        for x, y, a, r in zip(g, ga[:3], ga[3:6], ga[6:]):
+            np.testing.assert_array_equal(x, y)
+            assert np.all(np.abs(x) <= a + 1e-12)
+            assert np.all(r <= a + 1e-12)                      # root-sum-square <= sum of magnitudes
+        pos = np.abs(do)
+        dv, adv = attention_bwd_ref(q, k, v, pos, causal=causal, scale=0.3, abs_terms=True)[2:6:3]
+        np.testing.assert_allclose(dv, adv, rtol=1e-13, atol=1e-15)
+
+
+def test_sensitivity_bounds_rounding_of_o_in_d():
+    # Rounding O to bf16 inside D = dO . O moves dQ and dK by at most u * (sensitivity):
+    # recompute the gradients with D from a bf16-rounded O and compare.
+    from oracle.attention import visible_keys as vk
+    from synth import bf16_rne_bits
+    q, k, v, do = _inputs(1, 24, 24, 2, 1, 16, seed=20, spread=2.5)
+    scale = -0.6                                               # peaked rows: dS = P (dP - D) cancels
+    dq, dk, dv, aq, ak, av = attention_bwd_ref(q, k, v, do, causal=True, scale=scale, abs_terms=True)[:6]
+    O = attention_ref(q, k, v, causal=True, scale=scale)[0]
+    Ob = (bf16_rne_bits(O).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    sig = float(np.float32(scale))
+    gq = np.zeros_like(dq)
+    gk = np.zeros_like(dk)
+    for h in range(2):
+        for i in range(24):
+            n = vk(i, 24, 24, True)
+            s = sig * (k[0, :n, 0] @ q[0, i, h])
+            P = np.exp(s - s.max())
+            P /= P.sum()
+            dS = P * (v[0, :n, 0] @ do[0, i, h] - (do[0, i, h] * Ob[0, i, h]).sum())
+            gq[0, i, h] = sig * (dS @ k[0, :n, 0])
+            gk[0, :n, 0] += sig * np.outer(dS, q[0, i, h])
+    u = 2.0 ** -8
+    assert np.all(np.abs(gq - dq) <= u * aq + 1e-12)
+    assert np.all(np.abs(gk - dk) <= u * ak + 1e-12)
+    assert np.abs(gq - dq).max() > 1e-3                       # the effect is real, not negligible
+
+
+def test_rss_sensitivity_matches_simulated_rounding():
+    # Perturb every rounded factor by an independent relative error uniform in [-u, u]
+    # (dS, P, and each O element inside D) and compare the RMS change of the gradients
+    # with (u / sqrt(3)) times the oracle's root-sum-square sensitivity.
+    from oracle.attention import visible_keys as vk
+    B, Sq, Skv, Hq, Hkv, d = 1, 20, 20, 2, 1, 8
+    q, k, v, do = _inputs(B, Sq, Skv, Hq, Hkv, d, seed=21, spread=2.0)
+    scale, u, T = 0.55, 2.0 ** -8, 300
+    res = attention_bwd_ref(q, k, v, do, causal=True, scale=scale, abs_terms=True)
+    g, r = res[:3], res[6:]
+    rng = np.random.default_rng(22)
+    sq = [np.zeros_like(x) for x in g]
+    sig = float(np.float32(scale))
+    for _ in range(T):
+        gq, gk, gv = np.zeros_like(g[0]), np.zeros_like(g[1]), np.zeros_like(g[2])
+        for h in range(Hq):
+            for i in range(Sq):
+                n = vk(i, Sq, Skv, True)
+                s = sig * (k[0, :n, 0] @ q[0, i, h])
+                P = np.exp(s - s.max())
+                P /= P.sum()
+                O = P @ v[0, :n, 0]
+                Dp = (do[0, i, h] * O * (1 + u * rng.uniform(-1, 1, d))).sum()
+                dS = P * (v[0, :n, 0] @ do[0, i, h] - Dp) * (1 + u * rng.uniform(-1, 1, n))
+                Pp = P * (1 + u * rng.uniform(-1, 1, n))
+                gq[0, i, h] = sig * (dS @ k[0, :n, 0])
+                gk[0, :n, 0] += sig * np.outer(dS, q[0, i, h])
+                gv[0, :n, 0] += np.outer(Pp, do[0, i, h])
+        for acc, x, y in zip(sq, (gq, gk, gv), g):
+            acc += (x - y) ** 2
+    for acc, rr in zip(sq, r):
+        ratio = np.linalg.norm(np.sqrt(acc / T)) / np.linalg.norm(u / np.sqrt(3.0) * rr)
+        assert 0.9 < ratio < 1.1, ratio
