@@ -169,6 +169,39 @@ int fa_decode_paged(const void* q, const void* k_pages, const void* v_pages, con
                     int max_blocks_per_seq, int num_pages, float scale, int num_splits, void* workspace,
                     size_t workspace_bytes, void* stream);
 
+/*
+ * fa_bwd_workspace_bytes - bytes of device workspace fa_bwd needs: one fp32 per
+ * query row and head (D_i = dO_i . O_i), rounded up to 256. 0 for bad sizes.
+ */
+size_t fa_bwd_workspace_bytes(int B, int Hq, int Sq);
+
+/*
+ * fa_bwd - backward pass of exact attention: dQ, dK, dV for the forward of fa_fwd
+ * with the same q, k, v, causal flag and scale. The backward recomputes the
+ * attention probabilities instead of storing them ("Tracing Tiled QKV Data Movement
+ * in FlashAttention's Memory Hierarchy", Conclusion); the gradients are those of the
+ * forward's definition (chain rule through the row softmax):
+ *   P_ij = exp(scale * q_i.k_j - LSE_i) for visible j, D_i = dO_i . O_i,
+ *   dS_ij = P_ij (dO_i . v_j - D_i),
+ *   dV_j = sum_i P_ij dO_i, dK_j = scale sum_i dS_ij q_i, dQ_i = scale sum_j dS_ij k_j,
+ * where a KV head sums over every query head of its group (GQA).
+ *
+ *   q, o, dout, dq : bf16 [B, Sq, Hq, d]   (o and lse: outputs of fa_fwd)
+ *   k, v, dk, dv   : bf16 [B, Skv, Hkv, d]
+ *   lse            : fp32 [B, Hq, Sq], natural log (-inf for rows with no visible key)
+ *   workspace      : device memory of at least fa_bwd_workspace_bytes(B, Hq, Sq)
+ *                    bytes (overwritten; no state is kept between calls)
+ * All pointers are device memory, 16-byte aligned, caller-owned; outputs are fully
+ * overwritten (no accumulation into dq, dk, dv). Same shape and head-size rules as
+ * fa_fwd (d = 64 or 128, Hq % Hkv == 0); scale must be finite (any sign). Causal
+ * masking is aligned bottom-right as in fa_fwd. Rows with no visible key get dQ = 0.
+ * Two kernels run on `stream` in order (dQ and D, then dK and dV); nothing is
+ * allocated or synchronised. Returns FA_OK or an FA_ERR_* code before launching.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+           void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Skv, int d, int causal, float scale,
+           void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -180,3 +180,41 @@ def decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, 
                                      workspace.numel() * workspace.element_size(), _stream_ptr(q))
     _lib.check(st, "fa_decode_paged")
     return out, lse
+
+
+def bwd_workspace_bytes(B: int, Hq: int, Sq: int) -> int:
+    return int(_lib.load().fa_bwd_workspace_bytes(B, Hq, Sq))
+
+
+def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor,
+        causal: bool = False, scale=None, workspace: torch.Tensor | None = None, dq: torch.Tensor | None = None,
+        dk: torch.Tensor | None = None, dv: torch.Tensor | None = None):
+    """Attention backward (see fa_bwd in include/fa.h).
+
+    q, o, dout [B,Sq,Hq,d] bf16; k, v [B,Skv,Hkv,d] bf16; lse [B,Hq,Sq] fp32 from ``fwd``
+    -> (dq [B,Sq,Hq,d], dk, dv [B,Skv,Hkv,d]) bf16.
+    """
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _need(t, n, torch.bfloat16, 4)
+    _need(lse, "lse", torch.float32, 3)
+    B, Sq, Hq, d = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Skv, Hkv, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"k/v shape {tuple(k.shape)}/{tuple(v.shape)} does not match q {tuple(q.shape)}")
+    if tuple(o.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape) or tuple(lse.shape) != (B, Hq, Sq):
+        raise ValueError("o / dout / lse shapes do not match q")
+    if workspace is None:
+        workspace = torch.empty(bwd_workspace_bytes(B, Hq, Sq), dtype=torch.uint8, device=q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for t, n, shp in ((dq, "dq", q.shape), (dk, "dk", k.shape), (dv, "dv", k.shape)):
+        _need(t, n, torch.bfloat16, 4)
+        if tuple(t.shape) != tuple(shp):
+            raise ValueError(f"{n} has shape {tuple(t.shape)}, expected {tuple(shp)}")
+    st = _lib.load().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Sq, Skv, d,
+                            int(bool(causal)), _scale(scale, d), workspace.data_ptr(),
+                            workspace.numel() * workspace.element_size(), _stream_ptr(q))
+    _lib.check(st, "fa_bwd")
+    return dq, dk, dv

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = ["fa_fwd.hip", "fa_decode.hip", "fa_api.hip"]
+SOURCES = ["fa_fwd.hip", "fa_decode.hip", "fa_bwd.hip", "fa_api.hip"]
 # The kernel sources assume finite inputs (non-finite Q/K/V are unsupported), which
 # lets the compiler drop NaN canonicalisation around the softmax max. The C ABI source
 # keeps IEEE semantics for its argument checks (isfinite(scale)).

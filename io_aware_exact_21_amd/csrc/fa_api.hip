@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include "fa.h"
+#include "fa_bwd.hpp"
 #include "fa_launch.hpp"
 
 namespace {
@@ -266,6 +267,44 @@ int fa_decode_paged(const void* q, const void* k_pages, const void* v_pages, con
                                page_log2, max_blocks_per_seq, num_pages, scale, num_splits, s);
   if (st != FA_OK) return st;
   return combine_impl(part_o, part_lse, o, lse, B, Hq, d, num_splits, s);
+}
+
+size_t fa_bwd_workspace_bytes(int B, int Hq, int Sq) {
+  if (B < 1 || Hq < 1 || Sq < 1) return 0;
+  return align256((size_t)B * Hq * Sq * sizeof(float));
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
+           void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Skv, int d, int causal, float scale,
+           void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
+  int st = check_common(B, Hq, Hkv, Sq, Skv, d);
+  if (st != FA_OK) return st;
+  if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
+  if (!isfinite(scale)) return FA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+  if (!workspace || workspace_bytes < fa_bwd_workspace_bytes(B, Hq, Sq)) return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_ALIGN;
+  if (fa::bwd_dq_grid(B, Hq, Sq) > 0x7fffffffLL || fa::bwd_dkdv_grid(B, Hkv, Skv) > 0x7fffffffLL) return FA_ERR_SHAPE;
+  fa::BwdParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<const uint16_t*>(o);
+  p.dout = static_cast<const uint16_t*>(dout);
+  p.lse = lse;
+  p.dq = static_cast<uint16_t*>(dq);
+  p.dk = static_cast<uint16_t*>(dk);
+  p.dv = static_cast<uint16_t*>(dv);
+  p.dsum = static_cast<float*>(workspace);
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Sq = Sq; p.Skv = Skv; p.d = d;
+  p.scale = scale;
+  p.c = scale * 1.4426950408889634f;
+  (void)hipGetLastError();
+  if (fa::launch_bwd(p, causal != 0, static_cast<hipStream_t>(stream)) != hipSuccess) return FA_ERR_HIP;
+  return FA_OK;
 }
 
 }  // extern "C"

@@ -1,0 +1,483 @@
+// Backward pass of exact attention for gfx950 (CDNA4): dQ, dK and dV.
+//
+// The backward pass recomputes the attention probabilities from Q, K and the forward's
+// log-sum-exp instead of storing the attention matrix ("Tracing Tiled QKV Data Movement
+// in FlashAttention's Memory Hierarchy", Conclusion). With P_ij = exp(scale s_ij - LSE_i),
+// D_i = dO_i . O_i and dS_ij = P_ij (dO_i . V_j - D_i) the gradients are
+//     dV_j = sum_i P_ij dO_i,   dK_j = scale sum_i dS_ij Q_i,   dQ_i = scale sum_j dS_ij K_j.
+//
+// Two kernels, neither with atomics:
+//   * fa_bwd_dq_kernel: one workgroup per (batch, query head, 128 query rows). Q and dO
+//     of the wave's 32 rows stay in registers; K and V tiles stream through LDS. Per
+//     32-key unit it forms S^T = K Q^T and dP^T = V dO^T (a lane owns one query row),
+//     builds dS^T in registers and accumulates dQ^T += K^T dS^T. It also writes D.
+//   * fa_bwd_dkdv_kernel: one workgroup per (batch, KV head, 128 keys). K and V of the
+//     wave's 32 keys stay in registers; Q and dO tiles of every query head of the group
+//     stream through LDS with their LSE and D rows. Per 32-query unit it forms
+//     S = Q K^T and dP = dO V^T (a lane owns one key), and accumulates
+//     dV^T += dO^T P and dK^T += Q^T dS.
+// Splitting dQ from dK/dV costs two extra products per tile (S and dP are formed in
+// both kernels) but keeps every output written once by one workgroup.
+//
+// Tiles that are read both row-wise (MFMA A operand rows) and transposed
+// (ds_read_b64_tr_b16) use one XOR swizzle that is free of bank conflicts in both modes.
+#include "fa_bwd.hpp"
+#include "fa_device.hpp"
+
+namespace fa {
+
+namespace {
+
+constexpr int kBwdTile = 64;     // rows per streamed LDS tile
+constexpr int kBwdStages = 3;    // LDS ring depth (tiles)
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ const lds_u8* lds_ptr(unsigned a) { return (const lds_u8*)(uintptr_t)a; }
+
+// Wave-level direct global -> LDS copies (lane i's bytes at base + voff_i land at LDS
+// byte lds + i * size). Issued as inline assembly so the compiler does not order LDS
+// reads of other ring stages behind them; completion is tracked with wait_vmcnt plus a
+// barrier. m0 is written only here.
+__device__ __forceinline__ void dma16(const void* base, unsigned voff, unsigned lds) {
+  const unsigned m = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(m)
+               : "memory");
+}
+__device__ __forceinline__ void dma4(const void* base, unsigned voff, unsigned lds) {
+  const unsigned m = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(m)
+               : "memory");
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// 16-byte chunk c of tile row r is stored at chunk c ^ bswz(r). Row reads: 16 lanes
+// read 16 consecutive rows at one chunk, so bswz must permute 16 consecutive rows
+// onto distinct chunks (mod 16 for d = 128, per row parity for d = 64). Transposing
+// reads: 32 lanes read 4 consecutive rows x 64 contiguous bytes, so 4 consecutive
+// rows must differ in the swizzle bits above the 64-byte group.
+template <int D>
+__device__ __forceinline__ int bswz(int r) {
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
+// Per-lane LDS byte offsets inside one tile.
+template <int D>
+struct BwdGeom {
+  unsigned row[D / 16];   // A operand rows: tile row (lane % 32), chunk 2s + lane / 32
+  unsigned tr0[D / 32];   // transposing read, dim block db: rows 4 (lane/32) + (lane/4)%4
+  unsigned tr8[D / 32];   // the same rows + 8
+};
+
+template <int D>
+__device__ __forceinline__ BwdGeom<D> make_bgeom(int lane) {
+  BwdGeom<D> g;
+  const int lr = lane & 31, hh = lane >> 5;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) g.row[s] = 2u * (lr * D + (((2 * s + hh) ^ bswz<D>(lr)) << 3));
+  // ds_read_b64_tr_b16: in each group of 16 lanes, lane 4r+q fetches 4 consecutive
+  // dims of row r; lane i of the group then receives dim i of rows 0..3.
+  const int G = lane >> 4, r = (lane >> 2) & 3, q = lane & 3;
+  const int row0 = 4 * hh + r;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    const int dim0 = 32 * db + 16 * (G & 1) + 4 * q;
+    g.tr0[db] = 2u * (row0 * D + (((dim0 >> 3) ^ bswz<D>(row0)) << 3) + (dim0 & 7));
+    g.tr8[db] = 2u * ((row0 + 8) * D + (((dim0 >> 3) ^ bswz<D>(row0 + 8)) << 3) + (dim0 & 7));
+  }
+  return g;
+}
+
+// X B for 32 tile rows starting at LDS byte `base`: A = the rows (32 x 16 per step),
+// B = a resident operand (16 x 32 per step). Row lane%32 of the result is tile row
+// lane%32... in the accumulator layout each lane owns column lane % 32 of B.
+template <int D>
+__device__ __forceinline__ f32x16 mm_rows(unsigned base, const BwdGeom<D>& g, const u32x4 (&bop)[D / 16]) {
+  f32x16 s = {};
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) {
+    const u32x4 a = *reinterpret_cast<const lds_u32x4*>(lds_ptr(base + g.row[st]));
+    s = mfma_32x32x16(a, bop[st], s);
+  }
+  return s;
+}
+
+// acc[db] += X^T(dims of block db, tile rows 16t..16t+15) * B, for every dim block.
+// B is the bf16 operand built by p_operand from accumulator registers, whose row
+// order matches the rows the transposing read gives each lane.
+template <int D>
+__device__ __forceinline__ void mm_tr(unsigned base, int t, const BwdGeom<D>& g, u32x4 pb, f32x16 (&acc)[D / 32]) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    const unsigned off = base + (unsigned)(t * 16 * D * 2);
+    const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_ptr(off + g.tr0[db])));
+    const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_ptr(off + g.tr8[db])));
+    const u32x2 a0 = __builtin_bit_cast(u32x2, r0), a1 = __builtin_bit_cast(u32x2, r1);
+    const u32x4 a = {a0[0], a0[1], a1[0], a1[1]};
+    acc[db] = mfma_32x32x16(a, pb, acc[db]);
+  }
+}
+
+// Per-lane global byte offsets for the wave-level tile copies: copy n of wave w fills
+// tile rows KPI*(w + NW*n) ...; lane i takes row KPI*(w + NW*n) + i / CPR and fetches
+// global chunk (i % CPR) ^ bswz(row), so LDS chunk c of the row holds chunk c ^ bswz.
+template <int D, int NW>
+struct TileDma {
+  static constexpr int CPR = D / 8;
+  static constexpr int KPI = 64 / CPR;
+  static constexpr int NI = kBwdTile / KPI;
+  static constexpr int NPW = NI / NW;            // copies per wave and tensor
+  static_assert(NI % NW == 0, "copies must split evenly over the waves");
+  unsigned off[NPW];
+
+  __device__ __forceinline__ static int row_of(int n, int w, int lane) { return KPI * (w + NW * n) + lane / CPR; }
+
+  __device__ __forceinline__ void init(int64_t row_stride, int w, int lane) {
+#pragma unroll
+    for (int n = 0; n < NPW; ++n) {
+      const int r = row_of(n, w, lane);
+      off[n] = (unsigned)(r * row_stride * 2) + (((lane % CPR) ^ bswz<D>(r)) << 4);
+    }
+  }
+
+  // Copy tile rows [r0, r0 + 64) of a (row-strided) tensor into LDS byte `dst`. Rows at
+  // or past `rmax` re-read row rmax - 1 (finite data whose weight is masked to 0).
+  __device__ __forceinline__ void copy(const uint16_t* base, int64_t row_stride, int r0, int rmax, unsigned dst,
+                                       int w, int lane) const {
+    const uint16_t* t = base + (int64_t)r0 * row_stride;
+    if (r0 + kBwdTile <= rmax) {
+#pragma unroll
+      for (int n = 0; n < NPW; ++n) dma16(t, off[n], dst + (w + NW * n) * 1024);
+    } else {
+#pragma unroll
+      for (int n = 0; n < NPW; ++n) {
+        const int r = row_of(n, w, lane);
+        const unsigned ro = (unsigned)((int64_t)min(r, rmax - 1 - r0) * row_stride * 2);
+        dma16(t, ro + (((lane % CPR) ^ bswz<D>(r)) << 4), dst + (w + NW * n) * 1024);
+      }
+    }
+  }
+};
+
+__device__ __forceinline__ float bf16_lo(unsigned x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned x) { return __uint_as_float(x & 0xffff0000u); }
+
+// 4 consecutive fp32 values of an accumulator, scaled, to 4 bf16 at dst (8 bytes).
+__device__ __forceinline__ void store4(uint16_t* dst, const f32x16& a, int i, float sc) {
+  u32x2 v = {pack_bf16x2(a[4 * i] * sc, a[4 * i + 1] * sc), pack_bf16x2(a[4 * i + 2] * sc, a[4 * i + 3] * sc)};
+  *reinterpret_cast<u32x2*>(dst) = v;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------------------
+// dQ (and D): one workgroup per (batch, query head, kBwdRows query rows).
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdWaves * 64) void fa_bwd_dq_kernel(BwdParams p) {
+  constexpr int NW = kBwdWaves, BT = kBwdTile, NS = kBwdStages, BR = kBwdRows;
+  constexpr unsigned TB = BT * D * 2;                    // bytes per tile
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * NS * TB];   // K stages, then V stages
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 31, hh = lane >> 5;
+
+  // Workgroups go to the XCDs round-robin; head-major numbering keeps each head on one
+  // XCD (when the head count is a multiple of 8) and issues the heaviest causal query
+  // tiles first.
+  const int n_qt = (p.Sq + BR - 1) / BR;
+  const int heads = p.B * p.Hq;
+  const int rr = blockIdx.x / heads, hl = blockIdx.x - rr * heads;
+  const int qt = CAUSAL ? n_qt - 1 - rr : rr;
+  const int b = hl / p.Hq, h = hl - b * p.Hq;
+  const int hk = (h * p.Hkv) / p.Hq;
+  const int q0 = qt * BR;
+  const int diag = p.Skv - p.Sq;                         // row i sees keys j <= i + diag
+
+  int kend = p.Skv;                                      // keys any row of the workgroup sees
+  if (CAUSAL) kend = max(0, min(p.Skv, min(p.Sq, q0 + BR) + diag));
+  const int ntiles = (kend + BT - 1) / BT;
+
+  const int row = q0 + 32 * w + lr;
+  const bool valid = row < p.Sq;
+
+  // ---- resident Q and dO rows; D = dO . O ---------------------------------------------
+  u32x4 qop[D / 16], dop[D / 16];
+  float dsum = 0.f;
+  {
+    const int64_t off = ((int64_t)(b * p.Sq + (valid ? row : 0)) * p.Hq + h) * D + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      u32x4 zq = {0u, 0u, 0u, 0u}, zd = zq, zo = zq;
+      if (valid) {
+        zq = *reinterpret_cast<const u32x4*>(p.q + off + 16 * s);
+        zd = *reinterpret_cast<const u32x4*>(p.dout + off + 16 * s);
+        zo = *reinterpret_cast<const u32x4*>(p.o + off + 16 * s);
+      }
+      qop[s] = zq;
+      dop[s] = zd;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dsum += bf16_lo(zd[i]) * bf16_lo(zo[i]) + bf16_hi(zd[i]) * bf16_hi(zo[i]);
+    }
+  }
+  dsum = pair_sum(dsum);
+  const int64_t srow = ((int64_t)b * p.Hq + h) * p.Sq + row;
+  float lse2 = 0.f;
+  if (valid) {
+    if (hh == 0) p.dsum[srow] = dsum;
+    lse2 = p.lse[srow] * kLog2e;
+  }
+  if (!(lse2 > -INFINITY)) lse2 = 0.f;                   // a row that sees no key: every p is masked
+  wait_vmcnt<0>();                                       // only tile copies are in flight below
+
+  // ---- this wave's key range -----------------------------------------------------------
+  const int row_lo = q0 + 32 * w;
+  const int row_hi = min(row_lo + 31, p.Sq - 1);
+  int kw = row_lo < p.Sq ? p.Skv : 0;
+  if (CAUSAL && row_lo < p.Sq) kw = max(0, min(p.Skv, row_hi + diag + 1));
+  const int nu = (kw + 31) / 32;                         // 32-key units this wave computes
+  int umask = p.Skv / 32;                                // units below need no per-element mask
+  if (CAUSAL) umask = min(umask, max(0, row_lo + diag + 1) / 32);
+  const int lim = valid ? (CAUSAL ? min(p.Skv - 1, row + diag) : p.Skv - 1) : -1;
+  const float c = p.c;
+
+  const BwdGeom<D> g = make_bgeom<D>(lane);
+  const unsigned ring = lds_addr(smem);
+  const int64_t kv_stride = (int64_t)p.Hkv * D;
+  const uint16_t* kb = p.k + ((int64_t)b * p.Skv * p.Hkv + hk) * D;
+  const uint16_t* vb = p.v + ((int64_t)b * p.Skv * p.Hkv + hk) * D;
+  TileDma<D, NW> dma;
+  dma.init(kv_stride, w, lane);
+  constexpr int PER_TILE = 2 * TileDma<D, NW>::NPW;     // copies per wave and tile
+
+  auto issue = [&](int t) {
+    const unsigned st = (unsigned)(t % NS) * TB;
+    dma.copy(kb, kv_stride, t * BT, p.Skv, ring + st, w, lane);
+    dma.copy(vb, kv_stride, t * BT, p.Skv, ring + NS * TB + st, w, lane);
+  };
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
+
+  if (ntiles > 0) issue(0);
+  if (ntiles > 1) issue(1);
+  for (int j = 0; j < ntiles; ++j) {
+    if (j + 1 < ntiles) wait_vmcnt<PER_TILE>();          // tile j landed; tile j + 1 may be in flight
+    else wait_vmcnt<0>();
+    __syncthreads();                                     // every wave's share landed; tile j - 1 is free
+    if (j + 2 < ntiles) issue(j + 2);
+    const unsigned kst = ring + (unsigned)(j % NS) * TB;
+    const unsigned vst = kst + NS * TB;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int U = 2 * j + u;
+      if (U < nu) {
+        const f32x16 s = mm_rows<D>(kst + u * 32 * D * 2, g, qop);   // S^T: keys x queries
+        const f32x16 dp = mm_rows<D>(vst + u * 32 * D * 2, g, dop);  // dP^T
+        const bool masked = U >= umask;
+        f32x16 ds;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          float pe = fast_exp2(fmaf(s[e], c, -lse2));
+          if (masked && 32 * U + 8 * (e >> 2) + 4 * hh + (e & 3) > lim) pe = 0.f;
+          ds[e] = pe * (dp[e] - dsum);
+        }
+        mm_tr<D>(kst, 2 * u, g, p_operand(ds, 0), acc);
+        mm_tr<D>(kst, 2 * u + 1, g, p_operand(ds, 1), acc);
+      }
+    }
+  }
+
+  // ---- epilogue: dQ = scale * acc -------------------------------------------------------
+  if (valid) {
+    uint16_t* dst = p.dq + ((int64_t)(b * p.Sq + row) * p.Hq + h) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) store4(dst + 32 * db + 8 * i + 4 * hh, acc[db], i, p.scale);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// dK, dV: one workgroup per (batch, KV head, kBwdRows keys), over every query head of
+// the KV head's group.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdWaves * 64) void fa_bwd_dkdv_kernel(BwdParams p) {
+  constexpr int NW = kBwdWaves, BT = kBwdTile, NS = kBwdStages, BC = kBwdRows;
+  constexpr unsigned TB = BT * D * 2;                    // bytes per Q / dO tile
+  constexpr unsigned VB = BT * 4;                        // bytes per LSE / D tile
+  // Q stages, dO stages, LSE stages, D stages
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * NS * TB + 2 * NS * VB];
+  static_assert(NW % 2 == 0, "waves alternate between the LSE and D copies");
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 31, hh = lane >> 5;
+
+  // Low key tiles are seen by the most query rows under the causal mask; they come first.
+  const int heads = p.B * p.Hkv;
+  const int kt = blockIdx.x / heads, hl = blockIdx.x - kt * heads;
+  const int b = hl / p.Hkv, hk = hl - b * p.Hkv;
+  const int grp = p.Hq / p.Hkv;
+  const int k0 = kt * BC;
+  const int diag = p.Skv - p.Sq;
+
+  // query tiles that see any key of the workgroup (row i sees keys j <= i + diag)
+  const int nq_all = (p.Sq + BT - 1) / BT;
+  int qt0 = 0;
+  if (CAUSAL) qt0 = min(nq_all, max(0, k0 - diag) / BT);
+  const int nqt = nq_all - qt0;
+  const int n_it = nqt * grp;
+
+  const int key = k0 + 32 * w + lr;
+  const bool kvalid = key < p.Skv;
+  const int kw_lo = k0 + 32 * w;                         // first key of this wave
+
+  // ---- resident K and V rows -----------------------------------------------------------
+  u32x4 kop[D / 16], vop[D / 16];
+  {
+    const int64_t off = ((int64_t)(b * p.Skv + (kvalid ? key : 0)) * p.Hkv + hk) * D + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      u32x4 zk = {0u, 0u, 0u, 0u}, zv = zk;
+      if (kvalid) {
+        zk = *reinterpret_cast<const u32x4*>(p.k + off + 16 * s);
+        zv = *reinterpret_cast<const u32x4*>(p.v + off + 16 * s);
+      }
+      kop[s] = zk;
+      vop[s] = zv;
+    }
+  }
+  wait_vmcnt<0>();                                       // only tile copies are in flight below
+  const float c = p.c;
+
+  const BwdGeom<D> g = make_bgeom<D>(lane);
+  const unsigned ring = lds_addr(smem);
+  const unsigned lse_ring = ring + 2 * NS * TB;
+  const unsigned dsum_ring = lse_ring + NS * VB;
+  const int64_t q_stride = (int64_t)p.Hq * D;
+  TileDma<D, NW> dma;
+  dma.init(q_stride, w, lane);
+  constexpr int PER_IT = 2 * TileDma<D, NW>::NPW + 1;   // copies per wave and iteration
+  const unsigned row_off = (unsigned)lane * 4u;
+
+  auto issue = [&](int it) {
+    const int hq = hk * grp + it / nqt;
+    const int r0 = (qt0 + it % nqt) * BT;
+    const unsigned st = (unsigned)(it % NS);
+    const int64_t hoff = ((int64_t)b * p.Sq * p.Hq + hq) * D;
+    dma.copy(p.q + hoff, q_stride, r0, p.Sq, ring + st * TB, w, lane);
+    dma.copy(p.dout + hoff, q_stride, r0, p.Sq, ring + (NS + st) * TB, w, lane);
+    // LSE and D rows of the tile (rows past Sq re-read row Sq - 1)
+    const int64_t soff = ((int64_t)b * p.Hq + hq) * p.Sq + r0;
+    const unsigned ro = (unsigned)min(lane, p.Sq - 1 - r0) * 4u;
+    if ((w & 1) == 0) dma4(p.lse + soff, r0 + 64 <= p.Sq ? row_off : ro, lse_ring + st * VB);
+    else dma4(p.dsum + soff, r0 + 64 <= p.Sq ? row_off : ro, dsum_ring + st * VB);
+  };
+
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) {
+    dk[i] = f32x16{};
+    dv[i] = f32x16{};
+  }
+
+  if (n_it > 0) issue(0);
+  if (n_it > 1) issue(1);
+  for (int it = 0; it < n_it; ++it) {
+    if (it + 1 < n_it) wait_vmcnt<PER_IT>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+    if (it + 2 < n_it) issue(it + 2);
+    const unsigned st = (unsigned)(it % NS);
+    const unsigned qst = ring + st * TB, dst = ring + (NS + st) * TB;
+    const unsigned lst = lse_ring + st * VB, sst = dsum_ring + st * VB;
+    const int r0 = (qt0 + it % nqt) * BT;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int qu0 = r0 + 32 * u;                       // first query row of the unit
+      bool live = qu0 < p.Sq;
+      if (CAUSAL) live = live && min(qu0 + 31, p.Sq - 1) + diag >= kw_lo;
+      if (live) {
+        const f32x16 s = mm_rows<D>(qst + u * 32 * D * 2, g, kop);   // S: queries x keys
+        const f32x16 dp = mm_rows<D>(dst + u * 32 * D * 2, g, vop);  // dP
+        bool masked = qu0 + 31 >= p.Sq;
+        if (CAUSAL) masked = masked || qu0 + diag < kw_lo + 31;
+        f32x16 pr, ds;
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const unsigned ro = (unsigned)(32 * u + 8 * gq + 4 * hh) * 4u;
+          const f32x4 l4 = *reinterpret_cast<const lds_f32x4*>(lds_ptr(lst + ro));
+          const f32x4 d4 = *reinterpret_cast<const lds_f32x4*>(lds_ptr(sst + ro));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int e = 4 * gq + i;
+            float pe = fast_exp2(fmaf(s[e], c, -l4[i] * kLog2e));
+            if (masked) {
+              const int qi = qu0 + 8 * gq + 4 * hh + i;
+              if (qi >= p.Sq || (CAUSAL && key > qi + diag)) pe = 0.f;
+            }
+            pr[e] = pe;
+            ds[e] = pe * (dp[e] - d4[i]);
+          }
+        }
+        mm_tr<D>(dst, 2 * u, g, p_operand(pr, 0), dv);
+        mm_tr<D>(dst, 2 * u + 1, g, p_operand(pr, 1), dv);
+        mm_tr<D>(qst, 2 * u, g, p_operand(ds, 0), dk);
+        mm_tr<D>(qst, 2 * u + 1, g, p_operand(ds, 1), dk);
+      }
+    }
+  }
+
+  // ---- epilogue: dK = scale * acc, dV = acc ---------------------------------------------
+  if (kvalid) {
+    const int64_t obase = ((int64_t)(b * p.Skv + key) * p.Hkv + hk) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int dim = 32 * db + 8 * i + 4 * hh;
+        store4(p.dk + obase + dim, dk[db], i, p.scale);
+        store4(p.dv + obase + dim, dv[db], i, 1.f);
+      }
+  }
+}
+
+long long bwd_dq_grid(int B, int Hq, int Sq) { return (long long)B * Hq * ((Sq + kBwdRows - 1) / kBwdRows); }
+long long bwd_dkdv_grid(int B, int Hkv, int Skv) { return (long long)B * Hkv * ((Skv + kBwdRows - 1) / kBwdRows); }
+
+template <int D, bool CAUSAL>
+static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
+  const dim3 block(kBwdWaves * 64);
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)bwd_dq_grid(p.B, p.Hq, p.Sq)), block, 0, stream,
+                     p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)bwd_dkdv_grid(p.B, p.Hkv, p.Skv)), block, 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdParams& p, bool causal, hipStream_t stream) {
+  if (p.d == 128) return causal ? launch_bwd_t<128, true>(p, stream) : launch_bwd_t<128, false>(p, stream);
+  return causal ? launch_bwd_t<64, true>(p, stream) : launch_bwd_t<64, false>(p, stream);
+}
+
+}  // namespace fa

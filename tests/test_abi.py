@@ -25,7 +25,8 @@ def declared_functions():
 def test_header_declares_expected_entry_points():
     names = declared_functions()
     for n in ("fa_fwd", "fa_decode", "fa_decode_combine", "fa_decode_partials", "fa_decode_workspace_bytes",
-              "fa_decode_default_splits", "fa_status_string", "fa_fwd_f32out", "fa_decode_paged"):
+              "fa_decode_default_splits", "fa_status_string", "fa_fwd_f32out", "fa_decode_paged", "fa_bwd",
+              "fa_bwd_workspace_bytes"):
         assert n in names
 
 
@@ -145,3 +146,32 @@ def test_paged_decode_validation(lib):
     assert dec(wsb=need - 1) == FA_ERR_WORKSPACE
     assert dec(bt=A + 2) == FA_ERR_ALIGN
     assert dec(q=A + 8) == FA_ERR_ALIGN
+
+
+def test_bwd_validation(lib):
+    from io_aware_exact_21_amd._lib import (FA_ERR_ALIGN, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED,
+                                            FA_ERR_WORKSPACE)
+    need = lib.fa_bwd_workspace_bytes(2, 8, 100)
+    assert need == 2 * 8 * 100 * 4 + (256 - (2 * 8 * 100 * 4) % 256) % 256
+    assert lib.fa_bwd_workspace_bytes(0, 8, 100) == 0
+
+    def bwd(q=A, lse=A, dq=A, dk=A, ws=A, wsb=None, Hq=8, Hkv=2, Sq=100, Skv=90, d=128, causal=1,
+            scale=0.1):
+        return lib.fa_bwd(q, A, A, A, lse, A, dq, dk, A, 2, Hq, Hkv, Sq, Skv, d, causal, scale, ws,
+                          need if wsb is None else wsb, None)
+    assert bwd(q=None) == FA_ERR_NULL
+    assert bwd(lse=None) == FA_ERR_NULL
+    assert bwd(dq=None) == FA_ERR_NULL
+    assert bwd(dk=None) == FA_ERR_NULL
+    assert bwd(Hq=7) == FA_ERR_SHAPE
+    assert bwd(Sq=0) == FA_ERR_SHAPE
+    assert bwd(Skv=0) == FA_ERR_SHAPE
+    assert bwd(causal=2) == FA_ERR_SHAPE
+    assert bwd(scale=float("nan")) == FA_ERR_SHAPE
+    assert bwd(scale=float("inf")) == FA_ERR_SHAPE
+    assert bwd(d=96) == FA_ERR_UNSUPPORTED
+    assert bwd(ws=None) == FA_ERR_WORKSPACE
+    assert bwd(wsb=need - 1) == FA_ERR_WORKSPACE
+    assert bwd(q=A + 8) == FA_ERR_ALIGN
+    assert bwd(lse=A + 4) == FA_ERR_ALIGN
+    assert bwd(ws=A + 16 + 8) == FA_ERR_ALIGN
