@@ -29,7 +29,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 # Sources each kernel family is built from: an HBM-traffic record is used only while
 # the sources it was measured on are unchanged.
 KERNEL_SOURCES = {"fwd": ["fa_device.hpp", "fa_launch.hpp", "fa_fwd.hip"],
-                  "decode": ["fa_device.hpp", "fa_launch.hpp", "fa_decode.hip"]}
+                  "decode": ["fa_device.hpp", "fa_launch.hpp", "fa_decode.hip"],
+                  "bwd": ["fa_device.hpp", "fa_bwd.hpp", "fa_bwd.hip"]}
 
 
 def fwd_flops(w) -> float:
@@ -146,6 +147,53 @@ def paged_decode_bench(fa, dev, stream, steps: int, warmup: int) -> dict:
             "note": "fa_decode_paged (partials + merge) timed with HIP events around the whole call"}
 
 
+def backward_bench(fa, lib, stream, wkey: str, w, tq, tk, tv, o, lse, steps: int, warmup: int) -> dict:
+    """fa_bwd (dQ kernel + dK/dV kernel) on the forward workload, timed on its own.
+
+    TFLOP/s counts the five products of the backward (S = Q K^T, dP = dO V^T, dV, dK,
+    dQ), i.e. 2.5x the forward's FLOPs, causal halved; the kernels execute seven (S and
+    dP are formed in both kernels), which the rate does not count.
+    """
+    import numpy as np
+    import torch
+    from synth import make_grad_out
+
+    print(f"[bench] backward on {w.name}", file=sys.stderr, flush=True)
+    do = make_grad_out(w.B, w.Sq, w.Hq, w.d, w.seed)
+    tdo = torch.from_numpy(np.ascontiguousarray(do).view(np.int16)).view(torch.bfloat16).to(tq.device)
+    del do
+    dq, dk, dv = torch.empty_like(tq), torch.empty_like(tk), torch.empty_like(tv)
+    nws = fa.bwd_workspace_bytes(w.B, w.Hq, w.Sq)
+    ws = torch.empty(nws, dtype=torch.uint8, device=tq.device)
+    sp = stream.cuda_stream
+
+    def call():
+        fa._lib.check(lib.fa_bwd(tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                 tdo.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), w.B, w.Hq, w.Hkv,
+                                 w.Sq, w.Skv, w.d, int(w.causal), w.scale, ws.data_ptr(), nws, sp), "fa_bwd")
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = 2.5 * fwd_flops(w)
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"config": {**w.describe(), "seed": w.seed, "dO": "i.i.d. N(0,1) bf16, tensor id 5"},
+            "value": round(tflops, 2), "unit": "TFLOP/s", "ms": round(ms, 4),
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_BF16_TFLOPS, 4),
+                         "traffic": measured_traffic(f"fa_bwd_{wkey}_hbm_traffic.txt", "bwd"),
+                         "kernel": "fa_bwd_dq_kernel + fa_bwd_dkdv_kernel (one fa_bwd call)",
+                         "algorithmic_flops": flops, "executed_products": 7, "counted_products": 5},
+            "note": "fa_bwd timed with HIP events around the whole call on the library's stream"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -156,6 +204,7 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle CPU time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-paged", action="store_true", help="skip the paged-cache decode measurement")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward measurement")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run plain device copies of MIB MiB (reference reading for the HBM byte counters)")
     args = ap.parse_args()
@@ -272,6 +321,9 @@ def main() -> int:
         "wall_s_timed": round(t_wall, 3),
         "kernel_source_hash": {f: kernel_source_hash(f) for f in KERNEL_SOURCES},
     }
+    if not args.no_bwd:
+        rec["backward"] = backward_bench(fa, lib, stream, args.fwd_workload, wf, tq, tk, tv, o, lse, args.steps,
+                                         args.warmup)
     if not args.no_paged:
         rec["paged_decode"] = paged_decode_bench(fa, dev, stream, args.steps, args.warmup)
 

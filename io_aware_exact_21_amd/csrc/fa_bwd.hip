@@ -7,7 +7,7 @@
 //     dV_j = sum_i P_ij dO_i,   dK_j = scale sum_i dS_ij Q_i,   dQ_i = scale sum_j dS_ij K_j.
 //
 // Two kernels, neither with atomics:
-//   * fa_bwd_dq_kernel: one workgroup per (batch, query head, 128 query rows). Q and dO
+//   * fa_bwd_dq_kernel: one workgroup per (batch, query head, 256 query rows). Q and dO
 //     of the wave's 32 rows stay in registers; K and V tiles stream through LDS. Per
 //     32-key unit it forms S^T = K Q^T and dP^T = V dO^T (a lane owns one query row),
 //     builds dS^T in registers and accumulates dQ^T += K^T dS^T. It also writes D.
@@ -134,6 +134,42 @@ __device__ __forceinline__ void mm_tr(unsigned base, int t, const BwdGeom<D>& g,
   }
 }
 
+// The same two products with every LDS operand read issued before the first MFMA
+// that uses it (the register room of one wave per SIMD hides the LDS latency).
+template <int D>
+struct RowOps {
+  u32x4 a[D / 16];
+};
+template <int D>
+__device__ __forceinline__ RowOps<D> load_rows(unsigned base, const BwdGeom<D>& g) {
+  RowOps<D> r;
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) r.a[st] = *reinterpret_cast<const lds_u32x4*>(lds_ptr(base + g.row[st]));
+  return r;
+}
+template <int D>
+struct TrOps {
+  u32x4 a[D / 32];
+};
+template <int D>
+__device__ __forceinline__ TrOps<D> load_tr(unsigned base, int t, const BwdGeom<D>& g) {
+  TrOps<D> r;
+  const unsigned off = base + (unsigned)(t * 16 * D * 2);
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_ptr(off + g.tr0[db])));
+    const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_ptr(off + g.tr8[db])));
+    const u32x2 a0 = __builtin_bit_cast(u32x2, r0), a1 = __builtin_bit_cast(u32x2, r1);
+    r.a[db] = u32x4{a0[0], a0[1], a1[0], a1[1]};
+  }
+  return r;
+}
+template <int D>
+__device__ __forceinline__ void mm_tr_ops(const TrOps<D>& x, u32x4 pb, f32x16 (&acc)[D / 32]) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) acc[db] = mfma_32x32x16(x.a[db], pb, acc[db]);
+}
+
 // Per-lane global byte offsets for the wave-level tile copies: copy n of wave w fills
 // tile rows KPI*(w + NW*n) ...; lane i takes row KPI*(w + NW*n) + i / CPR and fetches
 // global chunk (i % CPR) ^ bswz(row), so LDS chunk c of the row holds chunk c ^ bswz.
@@ -187,10 +223,11 @@ __device__ __forceinline__ void store4(uint16_t* dst, const f32x16& a, int i, fl
 }  // namespace
 
 // ---------------------------------------------------------------------------------------
-// dQ (and D): one workgroup per (batch, query head, kBwdRows query rows).
+// dQ (and D): one workgroup per (batch, query head, kBwdDqRows query rows).
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdWaves * 64) void fa_bwd_dq_kernel(BwdParams p) {
-  constexpr int NW = kBwdWaves, BT = kBwdTile, NS = kBwdStages, BR = kBwdRows;
+__global__ __launch_bounds__(kBwdDqWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void fa_bwd_dq_kernel(BwdParams p) {
+  constexpr int NW = kBwdDqWaves, BT = kBwdTile, NS = kBwdStages, BR = kBwdDqRows;
   constexpr unsigned TB = BT * D * 2;                    // bytes per tile
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * NS * TB];   // K stages, then V stages
 
@@ -316,11 +353,11 @@ __global__ __launch_bounds__(kBwdWaves * 64) void fa_bwd_dq_kernel(BwdParams p) 
 }
 
 // ---------------------------------------------------------------------------------------
-// dK, dV: one workgroup per (batch, KV head, kBwdRows keys), over every query head of
-// the KV head's group.
+// dK, dV: one workgroup per (batch, KV head, kBwdDkvKeys keys), over every query head
+// of the KV head's group.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdWaves * 64) void fa_bwd_dkdv_kernel(BwdParams p) {
-  constexpr int NW = kBwdWaves, BT = kBwdTile, NS = kBwdStages, BC = kBwdRows;
+__global__ __launch_bounds__(kBwdDkvWaves * 64) void fa_bwd_dkdv_kernel(BwdParams p) {
+  constexpr int NW = kBwdDkvWaves, BT = kBwdTile, NS = kBwdStages, BC = kBwdDkvKeys;
   constexpr unsigned TB = BT * D * 2;                    // bytes per Q / dO tile
   constexpr unsigned VB = BT * 4;                        // bytes per LSE / D tile
   // Q stages, dO stages, LSE stages, D stages
@@ -410,39 +447,51 @@ __global__ __launch_bounds__(kBwdWaves * 64) void fa_bwd_dkdv_kernel(BwdParams p
     const unsigned qst = ring + st * TB, dst = ring + (NS + st) * TB;
     const unsigned lst = lse_ring + st * VB, sst = dsum_ring + st * VB;
     const int r0 = (qt0 + it % nqt) * BT;
-#pragma unroll
+    // One code path for every tile (no branch around the accumulator updates, so the
+    // accumulators stay in place across iterations); masks are applied in place. The
+    // two units run one after the other: unrolled, their operand prefetches together
+    // exceed the 256 architected VGPRs and the overflow costs more than it hides.
+#pragma unroll 1
     for (int u = 0; u < 2; ++u) {
       const int qu0 = r0 + 32 * u;                       // first query row of the unit
-      bool live = qu0 < p.Sq;
-      if (CAUSAL) live = live && min(qu0 + 31, p.Sq - 1) + diag >= kw_lo;
-      if (live) {
-        const f32x16 s = mm_rows<D>(qst + u * 32 * D * 2, g, kop);   // S: queries x keys
-        const f32x16 dp = mm_rows<D>(dst + u * 32 * D * 2, g, vop);  // dP
-        bool masked = qu0 + 31 >= p.Sq;
-        if (CAUSAL) masked = masked || qu0 + diag < kw_lo + 31;
-        f32x16 pr, ds;
+      const RowOps<D> aq = load_rows<D>(qst + u * 32 * D * 2, g);
+      const RowOps<D> ad = load_rows<D>(dst + u * 32 * D * 2, g);
+      f32x16 s = {}, dp = {};
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const unsigned ro = (unsigned)(32 * u + 8 * gq + 4 * hh) * 4u;
-          const f32x4 l4 = *reinterpret_cast<const lds_f32x4*>(lds_ptr(lst + ro));
-          const f32x4 d4 = *reinterpret_cast<const lds_f32x4*>(lds_ptr(sst + ro));
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int e = 4 * gq + i;
-            float pe = fast_exp2(fmaf(s[e], c, -l4[i] * kLog2e));
-            if (masked) {
-              const int qi = qu0 + 8 * gq + 4 * hh + i;
-              if (qi >= p.Sq || (CAUSAL && key > qi + diag)) pe = 0.f;
-            }
-            pr[e] = pe;
-            ds[e] = pe * (dp[e] - d4[i]);
-          }
-        }
-        mm_tr<D>(dst, 2 * u, g, p_operand(pr, 0), dv);
-        mm_tr<D>(dst, 2 * u + 1, g, p_operand(pr, 1), dv);
-        mm_tr<D>(qst, 2 * u, g, p_operand(ds, 0), dk);
-        mm_tr<D>(qst, 2 * u + 1, g, p_operand(ds, 1), dk);
+      for (int st = 0; st < D / 16; ++st) {
+        s = mfma_32x32x16(aq.a[st], kop[st], s);        // S: queries x keys
+        dp = mfma_32x32x16(ad.a[st], vop[st], dp);      // dP
       }
+      const TrOps<D> tv0 = load_tr<D>(dst, 2 * u, g), tv1 = load_tr<D>(dst, 2 * u + 1, g);
+      const TrOps<D> tq0 = load_tr<D>(qst, 2 * u, g), tq1 = load_tr<D>(qst, 2 * u + 1, g);
+      f32x16 pr, ds;
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const unsigned ro = (unsigned)(32 * u + 8 * gq + 4 * hh) * 4u;
+        const f32x4 l4 = *reinterpret_cast<const lds_f32x4*>(lds_ptr(lst + ro));
+        const f32x4 d4 = *reinterpret_cast<const lds_f32x4*>(lds_ptr(sst + ro));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = 4 * gq + i;
+          pr[e] = fast_exp2(fmaf(s[e], c, -l4[i] * kLog2e));
+          ds[e] = pr[e] * (dp[e] - d4[i]);
+        }
+      }
+      bool masked = qu0 + 31 >= p.Sq;
+      if (CAUSAL) masked = masked || qu0 + diag < kw_lo + 31;
+      if (masked) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int qi = qu0 + 8 * (e >> 2) + 4 * hh + (e & 3);
+          const bool off = qi >= p.Sq || (CAUSAL && key > qi + diag);
+          pr[e] = off ? 0.f : pr[e];
+          ds[e] = off ? 0.f : ds[e];
+        }
+      }
+      mm_tr_ops<D>(tv0, p_operand(pr, 0), dv);
+      mm_tr_ops<D>(tv1, p_operand(pr, 1), dv);
+      mm_tr_ops<D>(tq0, p_operand(ds, 0), dk);
+      mm_tr_ops<D>(tq1, p_operand(ds, 1), dk);
     }
   }
 
@@ -460,18 +509,19 @@ __global__ __launch_bounds__(kBwdWaves * 64) void fa_bwd_dkdv_kernel(BwdParams p
   }
 }
 
-long long bwd_dq_grid(int B, int Hq, int Sq) { return (long long)B * Hq * ((Sq + kBwdRows - 1) / kBwdRows); }
-long long bwd_dkdv_grid(int B, int Hkv, int Skv) { return (long long)B * Hkv * ((Skv + kBwdRows - 1) / kBwdRows); }
+long long bwd_dq_grid(int B, int Hq, int Sq) { return (long long)B * Hq * ((Sq + kBwdDqRows - 1) / kBwdDqRows); }
+long long bwd_dkdv_grid(int B, int Hkv, int Skv) {
+  return (long long)B * Hkv * ((Skv + kBwdDkvKeys - 1) / kBwdDkvKeys);
+}
 
 template <int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
-  const dim3 block(kBwdWaves * 64);
-  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)bwd_dq_grid(p.B, p.Hq, p.Sq)), block, 0, stream,
-                     p);
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)bwd_dq_grid(p.B, p.Hq, p.Sq)),
+                     dim3(kBwdDqWaves * 64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)bwd_dkdv_grid(p.B, p.Hkv, p.Skv)), block, 0,
-                     stream, p);
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)bwd_dkdv_grid(p.B, p.Hkv, p.Skv)),
+                     dim3(kBwdDkvWaves * 64), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -6,10 +6,13 @@
 
 namespace fa {
 
-// Waves per backward workgroup: the dQ kernel gives each wave 32 query rows, the
-// dK/dV kernel 32 keys.
-constexpr int kBwdWaves = 4;
-constexpr int kBwdRows = 32 * kBwdWaves;   // query rows (dQ) or keys (dK/dV) per workgroup
+// Waves per backward workgroup: the dQ kernel gives each wave 32 query rows (two
+// waves per SIMD), the dK/dV kernel 32 keys (one wave per SIMD: its dK and dV
+// accumulators alone take 128 registers per lane).
+constexpr int kBwdDqWaves = 8;
+constexpr int kBwdDkvWaves = 4;
+constexpr int kBwdDqRows = 32 * kBwdDqWaves;    // query rows per dQ workgroup
+constexpr int kBwdDkvKeys = 32 * kBwdDkvWaves;  // keys per dK/dV workgroup
 
 struct BwdParams {
   const uint16_t* q;      // [B, Sq, Hq, d]
