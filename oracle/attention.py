@@ -345,3 +345,34 @@ def attention_bwd_ref(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarra
         for n in (6, 7, 8):
             out[n] = np.sqrt(out[n])
     return tuple(out)
+
+
+def e4m3_value(codes: np.ndarray) -> np.ndarray:
+    """OCP fp8 e4m3 codes (uint8) -> float64, exactly.
+
+    Bit layout s eeee mmm, exponent bias 7: e = 0 gives the subnormals m * 2^-9,
+    otherwise (8 + m) * 2^(e - 10); 0x7F and 0xFF are NaN; there is no infinity.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    e = (c >> 3) & 15
+    m = c & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (8 + m) * np.ldexp(1.0, e - 10))
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return np.where(c >= 128, -mag, mag)
+
+
+def attention_fp8_ref(q8: np.ndarray, k8: np.ndarray, vt8: np.ndarray, q_scale: np.ndarray,
+                      k_scale: np.ndarray, v_scale: np.ndarray, *, causal: bool, scale: float):
+    """Exact attention of fp8-quantised inputs (the fp8 variant FlashAttention-3 adds).
+
+    [ILP, Deep dive] names an FP8 variant and nothing more; the reading is attention
+    on the dequantised tensors: Q = e4m3(q8) * q_scale[b, h], K likewise, and V from
+    the transposed codes vt8 [B, Hkv, d, ldv] (columns past Skv ignored). The result
+    is ``attention_ref`` on those float64 values.
+    q8 [B,Sq,Hq,d], k8 [B,Skv,Hkv,d] uint8; scales [B,H] -> O [B,Sq,Hq,d], LSE [B,Hq,Sq].
+    """
+    Skv = k8.shape[1]
+    Q = e4m3_value(q8) * np.asarray(q_scale, np.float64)[:, None, :, None]
+    K = e4m3_value(k8) * np.asarray(k_scale, np.float64)[:, None, :, None]
+    V = e4m3_value(vt8[..., :Skv]).transpose(0, 3, 1, 2) * np.asarray(v_scale, np.float64)[:, None, :, None]
+    return attention_ref(Q, K, V, causal=causal, scale=scale)
