@@ -202,6 +202,32 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Skv, int d, int causal, float scale,
            void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * fa_fwd_fp8 - exact attention forward on fp8 inputs (the FP8 variant that
+ * FlashAttention-3 adds: "FlashAttention & IO-aware attention", Deep dive). The
+ * result approximates softmax(scale * Q K^T) V of the dequantised tensors
+ *   Q = e4m3(q8) * q_scale[b, h],  K = e4m3(k8) * k_scale[b, hk],
+ *   V[b, j, hk, :] = e4m3(vt8[b, hk, :, j]) * v_scale[b, hk],
+ * with both products on the fp8 matrix cores (P rounded to e4m3 before the P.V
+ * product; the normaliser sums the unrounded probabilities).
+ *
+ *   q8   : e4m3 codes (OCP: sign, 4 exponent bits with bias 7, 3 mantissa bits; 0x7F
+ *          and 0xFF are NaN) [B, Sq, Hq, d]
+ *   k8   : e4m3 codes [B, Skv, Hkv, d]
+ *   vt8  : e4m3 codes of V transposed, [B, Hkv, d, ldv]; columns j < Skv are keys,
+ *          columns Skv .. ldv-1 are padding that must hold finite codes (zeros, say)
+ *   q_scale [B, Hq], k_scale [B, Hkv], v_scale [B, Hkv]: fp32 dequantisation scales
+ *   o    : bf16 [B, Sq, Hq, d];  lse: fp32 [B, Hq, Sq] natural log, or NULL
+ *   ldv  : multiple of 16, >= Skv rounded up to 16, with d * ldv <= 2e9
+ * d = 64 or 128, Hq % Hkv == 0, causal aligned bottom-right as in fa_fwd, scale finite.
+ * Device pointers: q8, k8, vt8, o, lse 16-byte aligned; the scales 4-byte aligned.
+ * Inputs must be finite. One launch on `stream`; nothing is allocated. Returns FA_OK or
+ * an FA_ERR_* code before launching.
+ */
+int fa_fwd_fp8(const void* q8, const void* k8, const void* vt8, const float* q_scale, const float* k_scale,
+               const float* v_scale, void* o, float* lse, int B, int Hq, int Hkv, int Sq, int Skv, int ldv, int d,
+               int causal, float scale, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

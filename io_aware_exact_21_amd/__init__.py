@@ -7,10 +7,11 @@ it loads libfa.so and fails loudly if the library is not built.
 """
 from . import _lib
 from .api import (bwd, bwd_workspace_bytes, decode, decode_chunk_bounds, decode_combine, decode_default_splits,
-                  decode_paged, decode_paged_default_splits, decode_partials, decode_workspace_bytes, fwd)
+                  decode_paged, decode_paged_default_splits, decode_partials, decode_workspace_bytes, fwd,
+                  fwd_fp8)
 
 _lib.load()
 
-__all__ = ["fwd", "bwd", "bwd_workspace_bytes", "decode", "decode_paged", "decode_paged_default_splits",
+__all__ = ["fwd", "fwd_fp8", "bwd", "bwd_workspace_bytes", "decode", "decode_paged", "decode_paged_default_splits",
            "decode_partials", "decode_combine", "decode_default_splits", "decode_workspace_bytes",
            "decode_chunk_bounds"]

@@ -218,3 +218,41 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse:
                             workspace.numel() * workspace.element_size(), _stream_ptr(q))
     _lib.check(st, "fa_bwd")
     return dq, dk, dv
+
+
+def fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, vt8: torch.Tensor, q_scale: torch.Tensor, k_scale: torch.Tensor,
+            v_scale: torch.Tensor, skv: int | None = None, causal: bool = False, scale=None,
+            out: torch.Tensor | None = None, lse: torch.Tensor | None = None, return_lse: bool = True):
+    """Attention forward on fp8 (e4m3) codes (see fa_fwd_fp8 in include/fa.h).
+
+    q8 [B,Sq,Hq,d], k8 [B,Skv,Hkv,d], vt8 [B,Hkv,d,ldv] uint8; q_scale [B,Hq], k_scale and
+    v_scale [B,Hkv] fp32 -> (o bf16 [B,Sq,Hq,d], lse fp32 [B,Hq,Sq]). ``skv`` defaults to
+    k8.shape[1].
+    """
+    _need(q8, "q8", torch.uint8, 4)
+    _need(k8, "k8", torch.uint8, 4)
+    _need(vt8, "vt8", torch.uint8, 4)
+    B, Sq, Hq, d = q8.shape
+    Skv, Hkv = k8.shape[1], k8.shape[2]
+    if skv is not None and skv != Skv:
+        raise ValueError("skv must equal k8.shape[1]")
+    if tuple(k8.shape) != (B, Skv, Hkv, d) or tuple(vt8.shape[:3]) != (B, Hkv, d):
+        raise ValueError("k8 / vt8 shapes do not match q8")
+    ldv = vt8.shape[3]
+    for t, n, shp in ((q_scale, "q_scale", (B, Hq)), (k_scale, "k_scale", (B, Hkv)), (v_scale, "v_scale", (B, Hkv))):
+        _need(t, n, torch.float32, 2)
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{n} has shape {tuple(t.shape)}, expected {shp}")
+    if out is None:
+        out = torch.empty((B, Sq, Hq, d), dtype=torch.bfloat16, device=q8.device)
+    _need(out, "out", torch.bfloat16, 4)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q8.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 3)
+    st = _lib.load().fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), vt8.data_ptr(), q_scale.data_ptr(),
+                                k_scale.data_ptr(), v_scale.data_ptr(), out.data_ptr(),
+                                lse.data_ptr() if lse is not None else None, B, Hq, Hkv, Sq, Skv, ldv, d,
+                                int(bool(causal)), _scale(scale, d), _stream_ptr(q8))
+    _lib.check(st, "fa_fwd_fp8")
+    return out, lse

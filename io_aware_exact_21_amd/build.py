@@ -15,11 +15,12 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = ["fa_fwd.hip", "fa_decode.hip", "fa_bwd.hip", "fa_api.hip"]
+SOURCES = ["fa_fwd.hip", "fa_decode.hip", "fa_bwd.hip", "fa_fwd_fp8.hip", "fa_api.hip"]
 # The kernel sources assume finite inputs (non-finite Q/K/V are unsupported), which
 # lets the compiler drop NaN canonicalisation around the softmax max. The C ABI source
 # keeps IEEE semantics for its argument checks (isfinite(scale)).
-KERNEL_ONLY_FLAGS = {"fa_fwd.hip": ["-fno-honor-nans"], "fa_decode.hip": ["-fno-honor-nans"]}
+KERNEL_ONLY_FLAGS = {"fa_fwd.hip": ["-fno-honor-nans"], "fa_decode.hip": ["-fno-honor-nans"],
+                     "fa_fwd_fp8.hip": ["-fno-honor-nans"]}
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

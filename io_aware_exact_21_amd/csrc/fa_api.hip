@@ -6,6 +6,7 @@
 
 #include "fa.h"
 #include "fa_bwd.hpp"
+#include "fa_fp8.hpp"
 #include "fa_launch.hpp"
 
 namespace {
@@ -304,6 +305,40 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
   p.c = scale * 1.4426950408889634f;
   (void)hipGetLastError();
   if (fa::launch_bwd(p, causal != 0, static_cast<hipStream_t>(stream)) != hipSuccess) return FA_ERR_HIP;
+  return FA_OK;
+}
+
+int fa_fwd_fp8(const void* q8, const void* k8, const void* vt8, const float* q_scale, const float* k_scale,
+               const float* v_scale, void* o, float* lse, int B, int Hq, int Hkv, int Sq, int Skv, int ldv, int d,
+               int causal, float scale, void* stream) {
+  if (!q8 || !k8 || !vt8 || !q_scale || !k_scale || !v_scale || !o) return FA_ERR_NULL;
+  int st = check_common(B, Hq, Hkv, Sq, Skv, d);
+  if (st != FA_OK) return st;
+  if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
+  if (!isfinite(scale)) return FA_ERR_SHAPE;
+  // V^T rows: at least Skv rounded up to 16 bytes, a multiple of 16, and small enough
+  // that d rows of one head stay within 32-bit byte offsets
+  if (ldv % 16 != 0 || ldv < (Skv + 15) / 16 * 16 || (double)ldv * d > 2.0e9) return FA_ERR_SHAPE;
+  if ((double)B * Hkv * d * ldv > 4.0e18) return FA_ERR_SHAPE;
+  if (!aligned16(q8) || !aligned16(k8) || !aligned16(vt8) || !aligned16(o) || (lse && !aligned16(lse)))
+    return FA_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(q_scale) | reinterpret_cast<uintptr_t>(k_scale) |
+       reinterpret_cast<uintptr_t>(v_scale)) & 3u)
+    return FA_ERR_ALIGN;
+  if (fa::fp8_grid_size(B, Hq, Sq) > 0x7fffffffLL) return FA_ERR_SHAPE;
+  fa::Fp8Params p;
+  p.q = static_cast<const uint8_t*>(q8);
+  p.k = static_cast<const uint8_t*>(k8);
+  p.vt = static_cast<const uint8_t*>(vt8);
+  p.q_scale = q_scale;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Sq = Sq; p.Skv = Skv; p.d = d; p.ldv = ldv;
+  p.c = scale * 1.4426950408889634f;
+  (void)hipGetLastError();
+  if (fa::launch_fwd_fp8(p, causal != 0, static_cast<hipStream_t>(stream)) != hipSuccess) return FA_ERR_HIP;
   return FA_OK;
 }
 

@@ -1,0 +1,37 @@
+// Direct global -> LDS copies and LDS addressing shared by the streaming kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+namespace dma {
+
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ const lds_u8* lds_ptr(unsigned a) { return (const lds_u8*)(uintptr_t)a; }
+
+// One wave-level copy: lane i's 16 bytes at base + voff_i land at LDS byte lds + 16 i
+// (base wave-uniform in SGPRs, lds wave-uniform in m0). Issued as inline assembly so
+// the compiler does not order later LDS reads of other ring stages behind it;
+// completion is tracked with wait_vmcnt plus a barrier. m0 is written only here.
+__device__ __forceinline__ void copy16(const void* base, unsigned voff, unsigned lds) {
+  const unsigned m = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(m)
+               : "memory");
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+}  // namespace dma
+}  // namespace fa

@@ -26,7 +26,7 @@ def test_header_declares_expected_entry_points():
     names = declared_functions()
     for n in ("fa_fwd", "fa_decode", "fa_decode_combine", "fa_decode_partials", "fa_decode_workspace_bytes",
               "fa_decode_default_splits", "fa_status_string", "fa_fwd_f32out", "fa_decode_paged", "fa_bwd",
-              "fa_bwd_workspace_bytes"):
+              "fa_bwd_workspace_bytes", "fa_fwd_fp8"):
         assert n in names
 
 
@@ -175,3 +175,23 @@ def test_bwd_validation(lib):
     assert bwd(q=A + 8) == FA_ERR_ALIGN
     assert bwd(lse=A + 4) == FA_ERR_ALIGN
     assert bwd(ws=A + 16 + 8) == FA_ERR_ALIGN
+
+
+def test_fwd_fp8_validation(lib):
+    from io_aware_exact_21_amd._lib import FA_ERR_ALIGN, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED
+
+    def f(q=A, vt=A, qs=A, o=A, lse=None, Hq=8, Hkv=2, Sq=100, Skv=90, ldv=96, d=128, causal=1, scale=0.1):
+        return lib.fa_fwd_fp8(q, A, vt, qs, A, A, o, lse, 2, Hq, Hkv, Sq, Skv, ldv, d, causal, scale, None)
+    assert f(q=None) == FA_ERR_NULL
+    assert f(vt=None) == FA_ERR_NULL
+    assert f(qs=None) == FA_ERR_NULL
+    assert f(o=None) == FA_ERR_NULL
+    assert f(Hq=7) == FA_ERR_SHAPE
+    assert f(ldv=80) == FA_ERR_SHAPE           # shorter than Skv rounded up to 16
+    assert f(ldv=100) == FA_ERR_SHAPE          # not a multiple of 16
+    assert f(causal=3) == FA_ERR_SHAPE
+    assert f(scale=float("nan")) == FA_ERR_SHAPE
+    assert f(d=96) == FA_ERR_UNSUPPORTED
+    assert f(q=A + 8) == FA_ERR_ALIGN
+    assert f(qs=A + 2) == FA_ERR_ALIGN
+    assert f(lse=A + 4) == FA_ERR_ALIGN
