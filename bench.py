@@ -25,12 +25,14 @@ sys.path.insert(0, ROOT)
 METRIC = "fwd attention TFLOP/s (bf16, causal-adjusted) & % MFMA peak; decode HBM GB/s"
 PEAK_MFMA_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0              # MI355X HBM3E
+PEAK_MFMA_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 PROFILES = os.path.join(ROOT, "profiles")
 # Sources each kernel family is built from: an HBM-traffic record is used only while
 # the sources it was measured on are unchanged.
 KERNEL_SOURCES = {"fwd": ["fa_device.hpp", "fa_launch.hpp", "fa_fwd.hip"],
                   "decode": ["fa_device.hpp", "fa_launch.hpp", "fa_decode.hip"],
-                  "bwd": ["fa_device.hpp", "fa_bwd.hpp", "fa_bwd.hip"]}
+                  "bwd": ["fa_device.hpp", "fa_bwd.hpp", "fa_bwd.hip"],
+                  "fp8": ["fa_device.hpp", "fa_dma.hpp", "fa_fp8.hpp", "fa_fwd_fp8.hip"]}
 
 
 def fwd_flops(w) -> float:
@@ -194,6 +196,54 @@ def backward_bench(fa, lib, stream, wkey: str, w, tq, tk, tv, o, lse, steps: int
             "note": "fa_bwd timed with HIP events around the whole call on the library's stream"}
 
 
+def fp8_bench(fa, stream, wkey: str, w, steps: int, warmup: int) -> dict:
+    """fa_fwd_fp8 on the e4m3-quantised version of the forward workload, timed on its own.
+
+    TFLOP/s counts 4 B Hq Sq Skv d (halved when causal), as for the bf16 forward; the
+    peak is the dense fp8 MFMA peak.
+    """
+    import numpy as np
+    import torch
+    from synth.fp8 import make_fp8_qkv
+
+    print(f"[bench] fp8 forward on {w.name}", file=sys.stderr, flush=True)
+    q8, k8, vt8, qs, ks, vs, ldv = make_fp8_qkv(w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.d, w.seed, w.k_stress_frac)
+    dev = torch.device("cuda:0")
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    tq, tk, tvt, tqs, tks, tvs = to(q8), to(k8), to(vt8), to(qs), to(ks), to(vs)
+    del q8, k8, vt8
+    o = torch.empty((w.B, w.Sq, w.Hq, w.d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
+    lib = fa._lib.load()
+    sp = stream.cuda_stream
+
+    def call():
+        fa._lib.check(lib.fa_fwd_fp8(tq.data_ptr(), tk.data_ptr(), tvt.data_ptr(), tqs.data_ptr(), tks.data_ptr(),
+                                     tvs.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B, w.Hq, w.Hkv, w.Sq, w.Skv,
+                                     ldv, w.d, int(w.causal), w.scale, sp), "fa_fwd_fp8")
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = fwd_flops(w)
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"config": {**w.describe(), "dtype_io": "e4m3 in, bf16 out", "layout": "q, k [B,S,H,d]; v [B,Hkv,d,S]",
+                       "quantisation": "per (batch, head) scale amax/448", "seed": w.seed},
+            "value": round(tflops, 2), "unit": "TFLOP/s", "ms": round(ms, 4),
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_FP8_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_FP8_TFLOPS, 4),
+                         "traffic": measured_traffic(f"fa_fwd_fp8_{wkey}_hbm_traffic.txt", "fp8"),
+                         "kernel": "fa_fwd_fp8_kernel", "algorithmic_flops": flops},
+            "note": "fa_fwd_fp8 timed with HIP events around the call on the library's stream"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -205,6 +255,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-paged", action="store_true", help="skip the paged-cache decode measurement")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward measurement")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 forward measurement")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run plain device copies of MIB MiB (reference reading for the HBM byte counters)")
     args = ap.parse_args()
@@ -324,6 +375,8 @@ def main() -> int:
     if not args.no_bwd:
         rec["backward"] = backward_bench(fa, lib, stream, args.fwd_workload, wf, tq, tk, tv, o, lse, args.steps,
                                          args.warmup)
+    if not args.no_fp8:
+        rec["fp8_forward"] = fp8_bench(fa, stream, args.fwd_workload, wf, args.steps, args.warmup)
     if not args.no_paged:
         rec["paged_decode"] = paged_decode_bench(fa, dev, stream, args.steps, args.warmup)
 

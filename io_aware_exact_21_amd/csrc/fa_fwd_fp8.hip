@@ -20,6 +20,10 @@
 //
 // Overflow: e4m3 has no infinity and converts values above 448 to NaN. The running max
 // moves whenever a row's scores exceed it by more than 2^8, so every p <= 256.
+//
+// The normaliser sums the unrounded fp32 p. (Summing the e4m3 P instead, on the matrix
+// cores against an all-ones operand, leaves the vector ALUs free of those additions but
+// moves the LSE by up to the e4m3 rounding of the few largest p: several hundredths.)
 #include "fa_device.hpp"
 #include "fa_dma.hpp"
 #include "fa_fp8.hpp"
@@ -171,8 +175,13 @@ __global__ __launch_bounds__(kFp8Waves * 64) void fa_fwd_fp8_kernel(Fp8Params p)
   if (CAUSAL) tmask = min(tmask, max(0, row_lo + diag + 1) / kTile);
   const int lim = valid ? (CAUSAL ? min(p.Skv - 1, row + diag) : p.Skv - 1) : -1;
 
-  // exponent factor: softmax scale * log2(e) * the Q and K dequantisation scales
-  const float c = p.c * p.q_scale[b * p.Hq + h] * p.k_scale[b * p.Hkv + hk];
+  // exponent factor: |softmax scale| * log2(e) * the Q and K dequantisation scales (the
+  // sign of the scale is folded into Q's sign bits, so the row max can be taken on the
+  // raw products); a zero scale zeroes Q, which makes every score exactly 0
+  const float qks = p.q_scale[b * p.Hq + h] * p.k_scale[b * p.Hkv + hk];
+  const float c = p.c == 0.f ? 1.f : fabsf(p.c) * qks;
+  const unsigned qsign = p.c < 0.f ? 0x80808080u : 0u;
+  const unsigned qmask = p.c == 0.f ? 0u : 0xFFFFFFFFu;
   const float vsc = p.v_scale[b * p.Hkv + hk];
 
   // ---- resident Q operand: row `row`, bytes 64 ks + 32 hh .. + 31 -------------------
@@ -186,29 +195,24 @@ __global__ __launch_bounds__(kFp8Waves * 64) void fa_fwd_fp8_kernel(Fp8Params p)
         z0 = *reinterpret_cast<const u32x4*>(qp + 64 * ks);
         z1 = *reinterpret_cast<const u32x4*>(qp + 64 * ks + 16);
       }
-      qop[ks] = join(z0, z1);
+      qop[ks] = join((z0 ^ qsign) & qmask, (z1 ^ qsign) & qmask);
     }
   }
   dma::wait_vmcnt<0>();                                  // only tile copies are in flight below
 
-  // ---- per-lane LDS offsets ---------------------------------------------------------------
-  unsigned kofs[2][D / 64][2];                           // S^T tile t, k-step, 16-byte half
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int r = key_of_row(t, lr);
+  // ---- per-lane LDS offsets: K rows of S^T tile 0 (tile 1 is 16 rows on, an immediate),
+  // V^T rows 32 db + lr (db steps are immediates)
+  unsigned kofs[D / 64][2];
+  {
+    const int r = key_of_row(0, lr);
 #pragma unroll
     for (int ks = 0; ks < D / 64; ++ks)
 #pragma unroll
-      for (int x = 0; x < 2; ++x) kofs[t][ks][x] = (unsigned)(r * D + (((4 * ks + 2 * hh + x) ^ kswz<D>(r)) << 4));
+      for (int x = 0; x < 2; ++x) kofs[ks][x] = (unsigned)(r * D + (((4 * ks + 2 * hh + x) ^ kswz<D>(r)) << 4));
   }
-  unsigned vofs[D / 32][2];                              // V^T rows 32 db + lr, keys 32 hh ..
+  unsigned vofs[2];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int r = 32 * db + lr;
-      vofs[db][x] = (unsigned)(r * 64 + (((2 * hh + x) ^ vswz(r)) << 4));
-    }
+  for (int x = 0; x < 2; ++x) vofs[x] = (unsigned)(lr * 64 + (((2 * hh + x) ^ vswz(lr)) << 4));
 
   const unsigned ring = dma::lds_addr(smem);
   const int kstride = p.Hkv * D;
@@ -222,45 +226,37 @@ __global__ __launch_bounds__(kFp8Waves * 64) void fa_fwd_fp8_kernel(Fp8Params p)
   for (int i = 0; i < D / 32; ++i) o[i] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  if (ntiles > 0) cp.issue(kb, vb, kstride, p.ldv, p.Skv, 0, ring, w, lane);
-  if (ntiles > 1) cp.issue(kb, vb, kstride, p.ldv, p.Skv, 1, ring, w, lane);
-  for (int j = 0; j < ntiles; ++j) {
-    if (j + 1 < ntiles) dma::wait_vmcnt<Fp8Dma<D, NW>::NPW>();
-    else dma::wait_vmcnt<0>();
-    __syncthreads();                                     // tile j landed everywhere; tile j - 1 is free
-    if (j + 2 < ntiles) cp.issue(kb, vb, kstride, p.ldv, p.Skv, j + 2, ring, w, lane);
-    if (j >= nt_w) continue;
-    const unsigned kst = ring + (unsigned)(j % kStages) * R::kTileBytes;
-    const unsigned vst = kst + R::kVBase;
-
-    // S^T for the tile's 64 keys (two 32-key output tiles, rows permuted)
+  // one 64-key tile; MASK applies the causal / key-count limit per element (a runtime
+  // flag: two specialised copies of the body measured slower)
+  auto tile = [&](unsigned kst, unsigned vst, int j, bool MASK) {
+    unsigned ka[D / 64][2];
+#pragma unroll
+    for (int ks = 0; ks < D / 64; ++ks)
+#pragma unroll
+      for (int x = 0; x < 2; ++x) ka[ks][x] = kst + kofs[ks][x];
     f32x16 s0 = {}, s1 = {};
 #pragma unroll
     for (int ks = 0; ks < D / 64; ++ks) {
-      const i32x8 a0 = join(*reinterpret_cast<const lds_u32x4*>(dma::lds_ptr(kst + kofs[0][ks][0])),
-                            *reinterpret_cast<const lds_u32x4*>(dma::lds_ptr(kst + kofs[0][ks][1])));
-      const i32x8 a1 = join(*reinterpret_cast<const lds_u32x4*>(dma::lds_ptr(kst + kofs[1][ks][0])),
-                            *reinterpret_cast<const lds_u32x4*>(dma::lds_ptr(kst + kofs[1][ks][1])));
+      const i32x8 a0 = join(*reinterpret_cast<const lds_u32x4*>(dma::lds_ptr(ka[ks][0])),
+                            *reinterpret_cast<const lds_u32x4*>(dma::lds_ptr(ka[ks][1])));
+      const i32x8 a1 = join(*reinterpret_cast<const lds_u32x4*>(dma::lds_ptr(ka[ks][0]) + 16 * D),
+                            *reinterpret_cast<const lds_u32x4*>(dma::lds_ptr(ka[ks][1]) + 16 * D));
       s0 = mfma_fp8(a0, qop[ks], s0);
       s1 = mfma_fp8(a1, qop[ks], s1);
     }
-    // this lane's 32 keys: k0 + 32 hh + e (s0) and k0 + 32 hh + 16 + e (s1)
-    float x[32];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      x[e] = s0[e] * c;
-      x[16 + e] = s1[e] * c;
-    }
-    if (j >= tmask) {
+    // this lane's 32 keys: 64 j + 32 hh + e (s0, e < 16) and + 16 + e (s1)
+    if (MASK) {
       const int kl = 64 * j + 32 * hh;
 #pragma unroll
-      for (int e = 0; e < 32; ++e)
-        if (kl + e > lim) x[e] = -INFINITY;
+      for (int e = 0; e < 16; ++e) {
+        if (kl + e > lim) s0[e] = -INFINITY;
+        if (kl + 16 + e > lim) s1[e] = -INFINITY;
+      }
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 32; ++e) mx = fmaxf(mx, x[e]);
-    mx = pair_max(mx);
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fmaxf(s0[e], s1[e]));
+    mx = pair_max(mx) * c;
     const bool need = mx > m_run + kGap;
     if (__ballot(need)) {
       const float alpha = need ? fast_exp2(m_run - mx) : 1.f;   // m_run = -inf gives 0
@@ -272,22 +268,39 @@ __global__ __launch_bounds__(kFp8Waves * 64) void fa_fwd_fp8_kernel(Fp8Params p)
         for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
     }
     const float nm = m_run == -INFINITY ? 0.f : -m_run;
+    float pv[32];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      pv[e] = fast_exp2(fmaf(s0[e], c, nm));
+      pv[16 + e] = fast_exp2(fmaf(s1[e], c, nm));
+    }
     float ls = 0.f;
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      x[e] = fast_exp2(x[e] + nm);
-      ls += x[e];
-    }
+    for (int e = 0; e < 32; ++e) ls += pv[e];
     l_run += ls;
     i32x8 pb;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) pb[i] = (int)pack_fp8x4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
+    for (int i = 0; i < 8; ++i) pb[i] = (int)pack_fp8x4(pv[4 * i], pv[4 * i + 1], pv[4 * i + 2], pv[4 * i + 3]);
+    const unsigned va0 = vst + vofs[0], va1 = vst + vofs[1];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      const i32x8 a = join(*reinterpret_cast<const lds_u32x4*>(dma::lds_ptr(vst + vofs[db][0])),
-                           *reinterpret_cast<const lds_u32x4*>(dma::lds_ptr(vst + vofs[db][1])));
+      const i32x8 a = join(*reinterpret_cast<const lds_u32x4*>(dma::lds_ptr(va0) + db * 2048),
+                           *reinterpret_cast<const lds_u32x4*>(dma::lds_ptr(va1) + db * 2048));
       o[db] = mfma_fp8(a, pb, o[db]);
     }
+  };
+
+  if (ntiles > 0) cp.issue(kb, vb, kstride, p.ldv, p.Skv, 0, ring, w, lane);
+  if (ntiles > 1) cp.issue(kb, vb, kstride, p.ldv, p.Skv, 1, ring, w, lane);
+  for (int j = 0; j < ntiles; ++j) {
+    if (j + 1 < ntiles) dma::wait_vmcnt<Fp8Dma<D, NW>::NPW>();
+    else dma::wait_vmcnt<0>();
+    __syncthreads();                                     // tile j landed everywhere; tile j - 1 is free
+    if (j + 2 < ntiles) cp.issue(kb, vb, kstride, p.ldv, p.Skv, j + 2, ring, w, lane);
+    if (j >= nt_w) continue;
+    const unsigned kst = ring + (unsigned)(j % kStages) * R::kTileBytes;
+    const unsigned vst = kst + R::kVBase;
+    tile(kst, vst, j, j >= tmask);
   }
 
   // ---- epilogue: O = v_scale * acc / l, LSE = ln2 * (m + log2 l) -------------------------
