@@ -376,3 +376,28 @@ def attention_fp8_ref(q8: np.ndarray, k8: np.ndarray, vt8: np.ndarray, q_scale: 
     K = e4m3_value(k8) * np.asarray(k_scale, np.float64)[:, None, :, None]
     V = e4m3_value(vt8[..., :Skv]).transpose(0, 3, 1, 2) * np.asarray(v_scale, np.float64)[:, None, :, None]
     return attention_ref(Q, K, V, causal=causal, scale=scale)
+
+
+def ffn_ref(h: np.ndarray, w1: np.ndarray, b1: np.ndarray, w2: np.ndarray, b2: np.ndarray) -> np.ndarray:
+    """Position-wise feed-forward network on rows h [..., d_model] (float64).
+
+    [IOP, Blockwise Parallel Transformers] applies the transformer's feed-forward
+    network to the attention output and notes that it acts on every token on its own.
+    The pages do not write the network out; the reading is the classic two-layer form
+    with a ReLU: relu(h W1 + b1) W2 + b2, W1 [d_model, d_ff], W2 [d_ff, d_model].
+    """
+    return np.maximum(h @ w1 + b1, 0.0) @ w2 + b2
+
+
+def bpt_layer_ref(q: np.ndarray, k: np.ndarray, v: np.ndarray, w1: np.ndarray, b1: np.ndarray, w2: np.ndarray,
+                  b2: np.ndarray, *, causal: bool, scale: float) -> np.ndarray:
+    """Attention followed by the feed-forward network, over the whole sequence.
+
+    [IOP, Blockwise Parallel Transformers]: the attention output of every query row,
+    heads concatenated (d_model = Hq * d), goes through ``ffn_ref``. The blockwise
+    schedule the pages describe computes this same function one query block at a time.
+    q [B,S,Hq,d], k, v [B,S,Hkv,d] -> y [B,S,Hq*d] (float64).
+    """
+    O, _ = attention_ref(q, k, v, causal=causal, scale=scale)
+    B, S, Hq, d = O.shape
+    return ffn_ref(O.reshape(B, S, Hq * d), w1, b1, w2, b2)

@@ -249,3 +249,26 @@ def make_paged_workload(w: PagedWorkload):
     lens = paged_seq_lens(w)
     return make_paged_decode(w.B, w.Hq, w.Hkv, w.d, w.page_size, lens, w.seed, w.spare_pages,
                              max_blocks=w.max_len // w.page_size)
+
+
+TENSOR_W1, TENSOR_B1, TENSOR_W2, TENSOR_B2 = 6, 7, 8, 9
+
+
+def _normal_2d(rows: int, cols: int, seed: int, tensor_id: int) -> np.ndarray:
+    out = np.empty((rows, cols), dtype=np.float64)
+    for n, r0 in enumerate(range(0, rows, ROWS_PER_BLOCK)):
+        rng = np.random.default_rng(np.random.SeedSequence(seed, spawn_key=(tensor_id, 0, n)))
+        out[r0:r0 + ROWS_PER_BLOCK] = rng.standard_normal(out[r0:r0 + ROWS_PER_BLOCK].shape)
+    return out
+
+
+def make_ffn_weights(d_model: int, d_ff: int, seed: int):
+    """Feed-forward weights as bf16 bits: W1 [d_model, d_ff], b1 [d_ff], W2 [d_ff, d_model],
+    b2 [d_model]. W1 and W2 are N(0,1) / sqrt(fan-in) (so activations stay of order one),
+    the biases N(0,1) / 10; blocks of 1024 rows seeded SeedSequence(seed, (id, 0, n)) with
+    ids 6, 7, 8, 9; rounded to bf16 (RNE)."""
+    w1 = bf16_rne_bits(_normal_2d(d_model, d_ff, seed, TENSOR_W1) / np.sqrt(d_model))
+    b1 = bf16_rne_bits(_normal_2d(1, d_ff, seed, TENSOR_B1)[0] / 10.0)
+    w2 = bf16_rne_bits(_normal_2d(d_ff, d_model, seed, TENSOR_W2) / np.sqrt(d_ff))
+    b2 = bf16_rne_bits(_normal_2d(1, d_model, seed, TENSOR_B2)[0] / 10.0)
+    return w1, b1, w2, b2
