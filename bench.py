@@ -244,6 +244,64 @@ def fp8_bench(fa, stream, wkey: str, w, steps: int, warmup: int) -> dict:
             "note": "fa_fwd_fp8 timed with HIP events around the call on the library's stream"}
 
 
+def bpt_bench(fa, stream, w, tq, tk, tv, steps: int, warmup: int, block_rows: int = 2048) -> dict:
+    """fa_bpt_layer (attention + feed-forward network, blockwise) on the forward workload
+    with d_model = Hq d and d_ff = 4 d_model, timed on its own; also the whole-sequence
+    schedule (one block per batch element) for comparison.
+
+    TFLOP/s counts the attention (as the forward, causal halved) plus the two FFN GEMMs,
+    4 B S d_model d_ff.
+    """
+    import numpy as np
+    import torch
+    from synth import make_ffn_weights
+
+    dm, dff = w.Hq * w.d, 4 * w.Hq * w.d
+    print(f"[bench] blockwise attention + FFN on {w.name}, d_ff {dff}", file=sys.stderr, flush=True)
+    dev = tq.device
+    up = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+    w1, b1, w2, b2 = (up(x) for x in make_ffn_weights(dm, dff, w.seed))
+    y = torch.empty((w.B, w.Sq, dm), dtype=torch.bfloat16, device=dev)
+    lib = fa._lib.load()
+    sp = stream.cuda_stream
+    flops = fwd_flops(w) + 4.0 * w.B * w.Sq * dm * dff
+
+    def timed(rows):
+        nws = fa.bpt_workspace_bytes(min(rows, w.Sq), w.Hq, w.d, dff)
+        ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+
+        def call():
+            fa._lib.check(lib.fa_bpt_layer(tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), w1.data_ptr(), b1.data_ptr(),
+                                           w2.data_ptr(), b2.data_ptr(), y.data_ptr(), w.B, w.Hq, w.Hkv, w.Sq, w.d,
+                                           dff, int(w.causal), w.scale, rows, ws.data_ptr(), nws, sp),
+                          "fa_bpt_layer")
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps, nws
+
+    ms, nws = timed(block_rows)
+    ms_full, nws_full = timed(w.Sq)
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"config": {**w.describe(), "d_model": dm, "d_ff": dff, "ffn": "relu(h W1 + b1) W2 + b2",
+                       "block_rows": block_rows, "weights": "N(0,1)/sqrt(fan-in), bias N(0,1)/10, bf16"},
+            "value": round(tflops, 2), "unit": "TFLOP/s", "ms": round(ms, 4),
+            "workspace_bytes": nws,
+            "whole_sequence_schedule": {"block_rows": w.Sq, "ms": round(ms_full, 4),
+                                        "TFLOP/s": round(flops / (ms_full * 1e-3) / 1e12, 2),
+                                        "workspace_bytes": nws_full},
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_BF16_TFLOPS, 4), "traffic": None,
+                         "kernel": "per block: fa_fwd_kernel + two hipBLASLt GEMMs", "algorithmic_flops": flops},
+            "note": "fa_bpt_layer timed with HIP events around the call on the library's stream"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -256,6 +314,7 @@ def main() -> int:
     ap.add_argument("--no-paged", action="store_true", help="skip the paged-cache decode measurement")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward measurement")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 forward measurement")
+    ap.add_argument("--no-bpt", action="store_true", help="skip the blockwise attention + FFN measurement")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run plain device copies of MIB MiB (reference reading for the HBM byte counters)")
     args = ap.parse_args()
@@ -375,6 +434,8 @@ def main() -> int:
     if not args.no_bwd:
         rec["backward"] = backward_bench(fa, lib, stream, args.fwd_workload, wf, tq, tk, tv, o, lse, args.steps,
                                          args.warmup)
+    if not args.no_bpt:
+        rec["blockwise_layer"] = bpt_bench(fa, stream, wf, tq, tk, tv, args.steps, args.warmup)
     if not args.no_fp8:
         rec["fp8_forward"] = fp8_bench(fa, stream, args.fwd_workload, wf, args.steps, args.warmup)
     if not args.no_paged:

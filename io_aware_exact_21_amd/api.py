@@ -256,3 +256,45 @@ def fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, vt8: torch.Tensor, q_scale: torc
                                 int(bool(causal)), _scale(scale, d), _stream_ptr(q8))
     _lib.check(st, "fa_fwd_fp8")
     return out, lse
+
+
+def bpt_workspace_bytes(block_rows: int, Hq: int, d: int, d_ff: int) -> int:
+    return int(_lib.load().fa_bpt_workspace_bytes(block_rows, Hq, d, d_ff))
+
+
+def bpt_layer(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w1: torch.Tensor, b1: torch.Tensor,
+              w2: torch.Tensor, b2: torch.Tensor, causal: bool = False, scale=None, block_rows: int = 2048,
+              workspace: torch.Tensor | None = None, out: torch.Tensor | None = None):
+    """Attention + feed-forward network, blockwise (see fa_bpt_layer in include/fa.h).
+
+    q [B,S,Hq,d], k/v [B,S,Hkv,d], w1 [Hq*d, d_ff], b1 [d_ff], w2 [d_ff, Hq*d], b2 [Hq*d], all
+    bf16 -> y bf16 [B, S, Hq*d].
+    """
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, torch.bfloat16, 4)
+    B, S, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if tuple(k.shape) != (B, S, Hkv, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k/v must be [B, S, Hkv, d] with q's B, S, d")
+    dm = Hq * d
+    _need(w1, "w1", torch.bfloat16, 2)
+    _need(w2, "w2", torch.bfloat16, 2)
+    _need(b1, "b1", torch.bfloat16, 1)
+    _need(b2, "b2", torch.bfloat16, 1)
+    d_ff = w1.shape[1]
+    if tuple(w1.shape) != (dm, d_ff) or tuple(w2.shape) != (d_ff, dm) or tuple(b1.shape) != (d_ff,) \
+            or tuple(b2.shape) != (dm,):
+        raise ValueError("feed-forward weights do not match d_model = Hq * d")
+    rows = min(block_rows, S)
+    need = bpt_workspace_bytes(rows, Hq, d, d_ff)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, S, dm), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", torch.bfloat16, 3)
+    st = _lib.load().fa_bpt_layer(q.data_ptr(), k.data_ptr(), v.data_ptr(), w1.data_ptr(), b1.data_ptr(),
+                                  w2.data_ptr(), b2.data_ptr(), out.data_ptr(), B, Hq, Hkv, S, d, d_ff,
+                                  int(bool(causal)), _scale(scale, d), block_rows, workspace.data_ptr(),
+                                  workspace.numel() * workspace.element_size(), _stream_ptr(q))
+    _lib.check(st, "fa_bpt_layer")
+    return out

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = ["fa_fwd.hip", "fa_decode.hip", "fa_bwd.hip", "fa_fwd_fp8.hip", "fa_api.hip"]
+SOURCES = ["fa_fwd.hip", "fa_decode.hip", "fa_bwd.hip", "fa_fwd_fp8.hip", "fa_bpt.hip", "fa_api.hip"]
 # The kernel sources assume finite inputs (non-finite Q/K/V are unsupported), which
 # lets the compiler drop NaN canonicalisation around the softmax max. The C ABI source
 # keeps IEEE semantics for its argument checks (isfinite(scale)).
@@ -60,7 +60,8 @@ def build(verbose: bool = False) -> str:
             if verbose and out.strip():
                 print(out)
     tmp = LIB + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
+    # hipBLASLt runs the feed-forward GEMMs of the blockwise transformer layer
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp, "-lhipblaslt"])
     os.replace(tmp, LIB)
     return LIB
 

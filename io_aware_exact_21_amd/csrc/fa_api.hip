@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include "fa.h"
+#include "fa_bpt.hpp"
 #include "fa_bwd.hpp"
 #include "fa_fp8.hpp"
 #include "fa_launch.hpp"
@@ -339,6 +340,60 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* vt8, const float* q_s
   p.c = scale * 1.4426950408889634f;
   (void)hipGetLastError();
   if (fa::launch_fwd_fp8(p, causal != 0, static_cast<hipStream_t>(stream)) != hipSuccess) return FA_ERR_HIP;
+  return FA_OK;
+}
+
+size_t fa_bpt_workspace_bytes(int block_rows, int Hq, int d, int d_ff) {
+  if (block_rows < 1 || Hq < 1 || d < 1 || d_ff < 1) return 0;
+  return align256((size_t)block_rows * Hq * d * 2) + align256((size_t)block_rows * d_ff * 2) + fa::kBptGemmWorkspace;
+}
+
+int fa_bpt_layer(const void* q, const void* k, const void* v, const void* w1, const void* b1, const void* w2,
+                 const void* b2, void* y, int B, int Hq, int Hkv, int S, int d, int d_ff, int causal, float scale,
+                 int block_rows, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !w1 || !b1 || !w2 || !b2 || !y) return FA_ERR_NULL;
+  int st = check_common(B, Hq, Hkv, S, S, d);
+  if (st != FA_OK) return st;
+  if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
+  if (d_ff < 1 || block_rows < 1 || (double)Hq * d * d_ff > 2.0e9 || (double)B * S * Hq * d > 4.0e18)
+    return FA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(w1) || !aligned16(b1) || !aligned16(w2) ||
+      !aligned16(b2) || !aligned16(y))
+    return FA_ERR_ALIGN;
+  const int rows_max = block_rows < S ? block_rows : S;
+  if (!workspace || workspace_bytes < fa_bpt_workspace_bytes(rows_max, Hq, d, d_ff)) return FA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return FA_ERR_ALIGN;
+  fa::FwdParams p;
+  p.k = nullptr;
+  st = scale_terms(scale, &p.c, &p.qsign, &p.qmask);
+  if (st != FA_OK) return st;
+  // workspace: attention output of one block [rows, Hq*d], its hidden activations
+  // [rows, d_ff], then the GEMM scratch
+  const int dm = Hq * d;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  uint16_t* attn = reinterpret_cast<uint16_t*>(ws);
+  uint16_t* mid = reinterpret_cast<uint16_t*>(ws + align256((size_t)rows_max * dm * 2));
+  void* gws = ws + align256((size_t)rows_max * dm * 2) + align256((size_t)rows_max * d_ff * 2);
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  for (int b = 0; b < B; ++b) {
+    for (int r0 = 0; r0 < S; r0 += rows_max) {
+      const int rows = S - r0 < rows_max ? S - r0 : rows_max;
+      // attention of the block's query rows: causal rows r0.. see keys up to their own
+      // position, which the bottom-right alignment gives with Skv = r0 + rows
+      p.q = static_cast<const uint16_t*>(q) + ((int64_t)b * S + r0) * Hq * d;
+      p.k = static_cast<const uint16_t*>(k) + (int64_t)b * S * Hkv * d;
+      p.v = static_cast<const uint16_t*>(v) + (int64_t)b * S * Hkv * d;
+      p.o = attn;
+      p.lse = nullptr;
+      p.B = 1; p.Hq = Hq; p.Hkv = Hkv; p.Sq = rows; p.Skv = causal ? r0 + rows : S; p.d = d;
+      if (fa::launch_fwd(p, causal != 0, false, hs) != hipSuccess) return FA_ERR_HIP;
+      // feed-forward network of the block: relu(attn W1 + b1) W2 + b2
+      if (fa::ffn_gemm(rows, d_ff, dm, attn, w1, b1, mid, true, gws, fa::kBptGemmWorkspace, hs)) return FA_ERR_HIP;
+      uint16_t* yb = static_cast<uint16_t*>(y) + ((int64_t)b * S + r0) * dm;
+      if (fa::ffn_gemm(rows, dm, d_ff, mid, w2, b2, yb, false, gws, fa::kBptGemmWorkspace, hs)) return FA_ERR_HIP;
+    }
+  }
   return FA_OK;
 }
 

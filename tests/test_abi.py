@@ -26,7 +26,8 @@ def test_header_declares_expected_entry_points():
     names = declared_functions()
     for n in ("fa_fwd", "fa_decode", "fa_decode_combine", "fa_decode_partials", "fa_decode_workspace_bytes",
               "fa_decode_default_splits", "fa_status_string", "fa_fwd_f32out", "fa_decode_paged", "fa_bwd",
-              "fa_bwd_workspace_bytes", "fa_fwd_fp8"):
+              "fa_bwd_workspace_bytes", "fa_fwd_fp8", "fa_bpt_layer",
+              "fa_bpt_workspace_bytes"):
         assert n in names
 
 
@@ -195,3 +196,27 @@ def test_fwd_fp8_validation(lib):
     assert f(q=A + 8) == FA_ERR_ALIGN
     assert f(qs=A + 2) == FA_ERR_ALIGN
     assert f(lse=A + 4) == FA_ERR_ALIGN
+
+
+def test_bpt_validation(lib):
+    from io_aware_exact_21_amd._lib import FA_ERR_ALIGN, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE
+    need = lib.fa_bpt_workspace_bytes(64, 4, 64, 1024)
+    assert need == 64 * 256 * 2 + 64 * 1024 * 2 + (32 << 20)
+    assert lib.fa_bpt_workspace_bytes(0, 4, 64, 1024) == 0
+
+    def f(q=A, w1=A, y=A, ws=A, wsb=None, Hq=4, Hkv=2, S=100, d=64, d_ff=1024, causal=1, rows=64):
+        return lib.fa_bpt_layer(q, A, A, w1, A, A, A, y, 2, Hq, Hkv, S, d, d_ff, causal, 0.1, rows, ws,
+                                need if wsb is None else wsb, None)
+    assert f(q=None) == FA_ERR_NULL
+    assert f(w1=None) == FA_ERR_NULL
+    assert f(y=None) == FA_ERR_NULL
+    assert f(Hq=3) == FA_ERR_SHAPE
+    assert f(d_ff=0) == FA_ERR_SHAPE
+    assert f(rows=0) == FA_ERR_SHAPE
+    assert f(causal=2) == FA_ERR_SHAPE
+    assert f(d=96) == FA_ERR_UNSUPPORTED
+    assert f(ws=None) == FA_ERR_WORKSPACE
+    assert f(wsb=need - 1) == FA_ERR_WORKSPACE
+    assert f(rows=128) == FA_ERR_WORKSPACE       # workspace sized for 64-row blocks
+    assert f(ws=A + 16) == FA_ERR_ALIGN
+    assert f(q=A + 8) == FA_ERR_ALIGN

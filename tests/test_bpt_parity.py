@@ -1,0 +1,125 @@
+"""GPU parity of the blockwise attention + feed-forward layer (fa_bpt_layer) against the
+fp64 oracle (bpt_layer_ref), through the C ABI.
+
+Tolerance, derived from the path's roundings (the stated bar covers attention outputs
+only): the attention output h reaches the first GEMM rounded to bf16 (relative 2^-8), the
+hidden activations m = relu(h W1 + b1) are rounded to bf16 after the ReLU (1-Lipschitz),
+and y once more. Each element of y is a sum of thousands of independently rounded terms,
+so its error is close to normal with standard deviation (2^-8 / sqrt 3) r,
+  r_n^2 = sum_j (sum_k h_k^2 W1_kj^2 + m_j^2) W2_jn^2   (root-sum-square sensitivity);
+per element |y' - y| <= 1e-2 + half a bf16 spacing of y + 6 sigma, and per tensor the
+forward's rel-L2 bar plus 2 ||sigma|| / ||y||. (The worst-case bound, sums of absolute
+values, reaches about 2 per element at d_model 4096 and would not catch an error in a
+single element.)
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle.attention import attention_ref, attention_rows, ffn_ref, kv_head_of, widen_bf16
+from synth import WORKLOADS, make_ffn_weights, make_qkv, make_workload
+from tests.parity import half_spacing_bf16, up
+
+pytestmark = pytest.mark.gpu
+U = 2.0 ** -8
+
+
+@pytest.fixture(scope="module")
+def fa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import io_aware_exact_21_amd as fa
+    return fa
+
+
+def _sigma(h, w1, b1, w2):
+    """Standard deviation of the rounding error of y, given fp64 h [n, dm] and the weights."""
+    m = np.maximum(h @ w1 + b1, 0.0)
+    r2 = ((h ** 2) @ (w1 ** 2) + m ** 2) @ (w2 ** 2)
+    return U / math.sqrt(3.0) * np.sqrt(r2)
+
+
+def _check(y_gpu, y, sigma, what="bpt"):
+    err = np.abs(y_gpu - y)
+    bound = 1e-2 + half_spacing_bf16(y) + 6.0 * sigma
+    idx = np.unravel_index(np.argmax(err / bound), err.shape)
+    assert np.isfinite(y_gpu).all(), f"{what}: non-finite output"
+    assert (err <= bound).all(), f"{what}: |err| {err[idx]:.4e} > bound {bound[idx]:.4e} at {idx}"
+    ny = np.linalg.norm(y)
+    rel = np.linalg.norm(y_gpu - y) / ny
+    rel_bound = 4e-3 + 2.0 * np.linalg.norm(sigma) / ny
+    assert rel <= rel_bound, f"{what}: rel-L2 {rel:.3e} > {rel_bound:.3e}"
+    return {"max_abs": float(err.max()), "max_err_over_bound": float((err / bound).max()), "rel_l2": float(rel),
+            "rel_l2_bound": float(rel_bound)}
+
+
+def _run(fa, q, k, v, w, causal, scale, block_rows):
+    tw = [up(x) for x in w]
+    y = fa.bpt_layer(up(q), up(k), up(v), *tw, causal=causal, scale=scale, block_rows=block_rows)
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy().astype(np.float64)
+
+
+SMALL = [
+    # B, Hq, Hkv, S, d, block_rows
+    (1, 2, 2, 100, 64, 64), (2, 2, 1, 130, 64, 32), (1, 4, 2, 257, 64, 100), (1, 2, 2, 200, 128, 200),
+    (1, 1, 1, 1, 64, 16), (2, 2, 2, 96, 64, 1000),
+]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SMALL, ids=[str(s) for s in SMALL])
+def test_small_shapes(fa, shape, causal):
+    B, Hq, Hkv, S, d, rows = shape
+    print(f"case {shape} causal={causal}", flush=True)
+    q, k, v = make_qkv(B, Hq, Hkv, S, S, d, seed=900 + S + d)
+    dm = Hq * d
+    w = make_ffn_weights(dm, 4 * dm, seed=901 + dm)
+    scale = 1.0 / math.sqrt(d)
+    y_gpu = _run(fa, q, k, v, w, causal, scale, rows)
+    W = [widen_bf16(x) for x in w]
+    O = attention_ref(widen_bf16(q), widen_bf16(k), widen_bf16(v), causal=causal, scale=scale)[0]
+    h = O.reshape(B * S, dm)
+    y = ffn_ref(h, *W).reshape(B, S, dm)
+    info = _check(y_gpu, y, _sigma(h, W[0], W[1], W[2]).reshape(B, S, dm))
+    print("  ", info, flush=True)
+
+
+def test_block_size_does_not_change_the_function(fa):
+    q, k, v = make_qkv(1, 2, 2, 300, 300, 64, seed=95)
+    w = make_ffn_weights(128, 512, seed=96)
+    a = _run(fa, q, k, v, w, True, 0.125, 64)
+    b = _run(fa, q, k, v, w, True, 0.125, 300)
+    W = [widen_bf16(x) for x in w]
+    O = attention_ref(widen_bf16(q), widen_bf16(k), widen_bf16(v), causal=True, scale=0.125)[0].reshape(300, 128)
+    y = ffn_ref(O, *W).reshape(1, 300, 128)
+    sig = _sigma(O, W[0], W[1], W[2]).reshape(1, 300, 128)
+    for yy in (a, b):
+        _check(yy, y, sig)
+
+
+def test_full_size_long_prefill_sampled(fa):
+    """Blockwise layer on the MHA long prefill (B2 H32 S8192 d128 causal, K x4 on 1% of
+    positions) with d_model 4096 and d_ff 16384, 2048-row blocks (the benchmark's
+    configuration); sampled rows of both batch elements against the oracle row by row."""
+    wl = WORKLOADS["mha8k"]
+    q, k, v = make_workload(wl)
+    dm = wl.Hq * wl.d
+    w = make_ffn_weights(dm, 4 * dm, seed=wl.seed)
+    print(f"full-size blockwise layer {wl.name}, d_ff {4 * dm}", flush=True)
+    y_gpu = _run(fa, q, k, v, w, True, wl.scale, 2048)
+    W = [widen_bf16(x) for x in w]
+    rng = np.random.default_rng(97)
+    for b in range(wl.B):
+        rows = np.unique(np.concatenate([[0, 1, 2047, 2048, wl.Sq - 1], rng.integers(0, wl.Sq, 27)]))
+        h = np.zeros((len(rows), dm))
+        for hq in range(wl.Hq):
+            hk = kv_head_of(hq, wl.Hq, wl.Hkv)
+            o, _ = attention_rows(widen_bf16(q[b, rows, hq]), widen_bf16(k[b, :, hk]), widen_bf16(v[b, :, hk]), rows,
+                                  wl.Sq, True, wl.scale)
+            h[:, hq * wl.d:(hq + 1) * wl.d] = o
+        y = ffn_ref(h, *W)
+        info = _check(y_gpu[b, rows], y, _sigma(h, W[0], W[1], W[2]))
+        print("  ", b, info, flush=True)
