@@ -155,26 +155,6 @@ __device__ __forceinline__ void pv_unit(const unsigned (&va)[D / 32], unsigned i
   }
 }
 
-// Interleave of one slot (P.V of one unit, Q.K^T of a later unit, softmax of the unit
-// in between): every MFMA is followed by the next operand reads and a share of the
-// softmax VALU work. Scheduling hints only; they do not change what is computed.
-#define FA_SG(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
-#define FA_SG_MFMA 0x008
-#define FA_SG_DSRD 0x100
-#define FA_SG_VALU 0x402   // VALU incl. transcendentals
-#define FA_SG_STEP(nrd, nv) FA_SG(FA_SG_MFMA, 1); FA_SG(FA_SG_DSRD, nrd); FA_SG(FA_SG_VALU, nv)
-template <int D>
-__device__ __forceinline__ void slot_schedule() {
-  FA_SG(FA_SG_DSRD, 4);
-  FA_SG_STEP(2, 4); FA_SG_STEP(2, 4); FA_SG_STEP(2, 4); FA_SG_STEP(2, 4);
-  FA_SG_STEP(2, 4); FA_SG_STEP(2, 4); FA_SG_STEP(1, 4); FA_SG_STEP(1, 4);
-  if (D == 128) {
-    FA_SG_STEP(1, 4); FA_SG_STEP(1, 4); FA_SG_STEP(1, 4); FA_SG_STEP(1, 4);
-    FA_SG_STEP(1, 4); FA_SG_STEP(1, 4); FA_SG_STEP(0, 4); FA_SG_STEP(0, 4);
-  }
-}
-#undef FA_SG_STEP
-
 __device__ __forceinline__ unsigned bf16_pair_sum_weights() { return 0x3F803F80u; }   // (1.0, 1.0)
 
 // Online-softmax step of one 32-row group over one 32-key unit. `s` holds this lane's
@@ -218,30 +198,6 @@ __device__ __forceinline__ void softmax_unit(f32x16 s, float& m, float& l, float
   l = fmaf(l, alpha, ls);
 }
 
-// Softmax step without a max reduction, for units whose row already has a finite
-// running max m: p = 2^(s*c - m) packed to bf16, and this lane's sum of the rounded p in
-// `ls`. Every p is <= kRescaleBound whenever ls is, so the caller only has to redo the
-// unit with the full step (which may move m) when some lane's ls exceeds that bound;
-// the result is then the same as taking the full step directly.
-__device__ __forceinline__ void softmax_unit_nomax(const f32x16& s, float m, u32x4 (&pout)[2], float c,
-                                                   float& ls) {
-  const float nm = -m;
-  ls = 0.f;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    unsigned pk[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float a = fast_exp2(fmaf(s[8 * h + 2 * i], c, nm));
-      const float b = fast_exp2(fmaf(s[8 * h + 2 * i + 1], c, nm));
-      pk[i] = pack_bf16x2(a, b);
-      ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[i]),
-                                           __builtin_bit_cast(bf16x2, bf16_pair_sum_weights()), ls, false);
-    }
-    pout[h] = u32x4{pk[0], pk[1], pk[2], pk[3]};
-  }
-}
-
 // Per-wave state of the forward pass and its per-tile steps.
 template <int D, bool CAUSAL>
 struct FwdWave {
@@ -275,30 +231,85 @@ struct FwdWave {
     }
   }
 
+  // One hot-loop slot: Q.K^T of the unit two ahead into `sout`, then P.V of the unit in
+  // `pin`, with the softmax of the unit in between (`sin` -> `pout`) spread over them.
+  // One MFMA per step: a step first reads the operand of the MFMA two steps ahead, then
+  // issues its MFMA and a share of the softmax; a scheduling fence after every step keeps
+  // that order (the compiler's own schedule left most LDS reads exposed). Q.K^T goes first
+  // so that its dependent MFMA chain has finished long before the next slot's softmax
+  // reads the scores.
+  // The softmax step skips the max reduction: p = 2^(s*c - m) against the current running
+  // max, packed to bf16, with this lane's sum of the rounded p in `ls`. Every p is <=
+  // kRescaleBound whenever ls is, so when some lane's ls exceeds that bound the slot
+  // returns false and the caller redoes the unit with the full step (which may move m);
+  // the result is then the same as taking the full step directly.
+  __device__ __forceinline__ bool fast_slot(const unsigned (&ka)[D / 16], const unsigned (&va)[D / 32],
+                                            unsigned imm, const u32x4 (&pin)[2], f32x16& sout,
+                                            const f32x16& sin, u32x4 (&pout)[2]) {
+    constexpr int NDB = D / 32;
+    constexpr int NPV = 2 * NDB;          // P.V MFMAs (16-key step tt, dim block db)
+    constexpr int NQK = D / 16;           // Q.K^T MFMAs
+    constexpr int N = NPV + NQK;
+    constexpr int E = 16 / N;             // softmax elements per step
+    const float nm = -m;
+    float ls = 0.f;
+    u32x4 op[N];
+    float pe[16];
+    unsigned pk[8];
+    // steps [0, NQK): Q.K^T; steps [NQK, N): P.V
+    auto load = [&](int i) {
+      if (i >= NQK) {
+        const int tt = (i - NQK) / NDB, db = (i - NQK) % NDB;
+        const lds_u8* a0p = lds_ptr(va[db]) + imm + tt * 16 * D * 2;
+        const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0p));
+        const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0p + 8 * D * 2));
+        const u32x2 x0 = __builtin_bit_cast(u32x2, r0), x1 = __builtin_bit_cast(u32x2, r1);
+        op[i] = u32x4{x0[0], x0[1], x1[0], x1[1]};
+      } else {
+        op[i] = *reinterpret_cast<const lds_u32x4*>(lds_ptr(ka[i]) + imm);
+      }
+    };
+    load(0);
+    load(1);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 s = {};
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      if (i + 2 < N) load(i + 2);
+      if (i >= NQK) {
+        const int tt = (i - NQK) / NDB, db = (i - NQK) % NDB;
+        o[db] = mfma_32x32x16(op[i], pin[tt], o[db]);
+      } else {
+        s = mfma_32x32x16(op[i], q[i], s);
+      }
+#pragma unroll
+      for (int e = E * i; e < E * i + E; ++e) {
+        pe[e] = fast_exp2(fmaf(sin[e], c, nm));
+        if (e & 1) {
+          pk[e >> 1] = pack_bf16x2(pe[e - 1], pe[e]);
+          ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[e >> 1]),
+                                               __builtin_bit_cast(bf16x2, bf16_pair_sum_weights()), ls, false);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    pout[0] = u32x4{pk[0], pk[1], pk[2], pk[3]};
+    pout[1] = u32x4{pk[4], pk[5], pk[6], pk[7]};
+    sout = s;
+    if (__ballot(!(ls <= kRescaleBound))) return false;
+    l += ls;
+    return true;
+  }
   // Slot A of tile j (units 2j .. 2j + 3 live, unmasked, finite running max): PV(2j),
   // QK(2j + 2) and the max-free softmax of unit 2j + 1. Returns false when some row's
   // probabilities exceed the bound (its max jumped); unit 2j + 1 must then be redone with
   // redo_a before slot B.
   __device__ __forceinline__ bool fast_slot_a(const unsigned (&ka)[D / 16], const unsigned (&va)[D / 32]) {
-    float ls;
-    pv_unit<D>(va, 0, p0, o);
-    s0 = qk_unit<D>(ka, 0, q);
-    softmax_unit_nomax(s1, m, p1, c, ls);
-    slot_schedule<D>();
-    if (__ballot(!(ls <= kRescaleBound))) return false;
-    l += ls;
-    return true;
+    return fast_slot(ka, va, 0, p0, s0, s1, p1);
   }
   // Slot B of tile j: PV(2j + 1), QK(2j + 3) and the max-free softmax of unit 2j + 2.
   __device__ __forceinline__ bool fast_slot_b(const unsigned (&ka)[D / 16], const unsigned (&va)[D / 32]) {
-    float ls;
-    pv_unit<D>(va, 32 * D * 2, p1, o);
-    s1 = qk_unit<D>(ka, 32 * D * 2, q);
-    softmax_unit_nomax(s0, m, p0, c, ls);
-    slot_schedule<D>();
-    if (__ballot(!(ls <= kRescaleBound))) return false;
-    l += ls;
-    return true;
+    return fast_slot(ka, va, 32 * D * 2, p1, s1, s0, p0);
   }
   // Redo the softmax of a unit with the full step (which moves the running max) and
   // rescale the accumulator. The unit's scores are formed again from its K tile, still

@@ -28,6 +28,8 @@
 #include "fa_dma.hpp"
 #include "fa_fp8.hpp"
 
+#include <type_traits>
+
 namespace fa {
 
 namespace {
@@ -226,9 +228,10 @@ __global__ __launch_bounds__(kFp8Waves * 64) void fa_fwd_fp8_kernel(Fp8Params p)
   for (int i = 0; i < D / 32; ++i) o[i] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // one 64-key tile; MASK applies the causal / key-count limit per element (a runtime
-  // flag: two specialised copies of the body measured slower)
-  auto tile = [&](unsigned kst, unsigned vst, int j, bool MASK) {
+  // one 64-key tile; MASK (a compile-time tag) applies the causal / key-count limit per
+  // element
+  auto tile = [&](unsigned kst, unsigned vst, int j, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     unsigned ka[D / 64][2];
 #pragma unroll
     for (int ks = 0; ks < D / 64; ++ks)
@@ -292,15 +295,26 @@ __global__ __launch_bounds__(kFp8Waves * 64) void fa_fwd_fp8_kernel(Fp8Params p)
 
   if (ntiles > 0) cp.issue(kb, vb, kstride, p.ldv, p.Skv, 0, ring, w, lane);
   if (ntiles > 1) cp.issue(kb, vb, kstride, p.ldv, p.Skv, 1, ring, w, lane);
-  for (int j = 0; j < ntiles; ++j) {
+  auto sync = [&](int j) {
     if (j + 1 < ntiles) dma::wait_vmcnt<Fp8Dma<D, NW>::NPW>();
     else dma::wait_vmcnt<0>();
     __syncthreads();                                     // tile j landed everywhere; tile j - 1 is free
     if (j + 2 < ntiles) cp.issue(kb, vb, kstride, p.ldv, p.Skv, j + 2, ring, w, lane);
+  };
+  // Tiles below tmask need no mask: one loop with the mask-free body, then the rest.
+  // Every wave passes one barrier per tile in either loop, so the barriers still match.
+  int j = 0;
+  const int split = min(tmask, min(nt_w, ntiles));
+  for (; j < split; ++j) {
+    sync(j);
+    const unsigned kst = ring + (unsigned)(j % kStages) * R::kTileBytes;
+    tile(kst, kst + R::kVBase, j, std::false_type{});
+  }
+  for (; j < ntiles; ++j) {
+    sync(j);
     if (j >= nt_w) continue;
     const unsigned kst = ring + (unsigned)(j % kStages) * R::kTileBytes;
-    const unsigned vst = kst + R::kVBase;
-    tile(kst, vst, j, j >= tmask);
+    tile(kst, kst + R::kVBase, j, std::true_type{});
   }
 
   // ---- epilogue: O = v_scale * acc / l, LSE = ln2 * (m + log2 l) -------------------------
