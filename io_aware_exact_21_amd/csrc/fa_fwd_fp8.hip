@@ -37,6 +37,9 @@ namespace {
 constexpr int kTile = 64;      // keys per LDS tile
 constexpr int kStages = 3;     // LDS ring depth
 constexpr float kGap = 8.0f;   // log2 units; keeps p <= 2^8 (e4m3 max is 448)
+// Bound of the max-free step: a lane's sum of its p bounds each of them, so a sum at or
+// below 2^8 keeps every p inside e4m3's finite range as the full step does.
+constexpr float kPBound = 256.0f;
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
@@ -256,31 +259,54 @@ __global__ __launch_bounds__(kFp8Waves * 64) void fa_fwd_fp8_kernel(Fp8Params p)
         if (kl + 16 + e > lim) s1[e] = -INFINITY;
       }
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fmaxf(s0[e], s1[e]));
-    mx = pair_max(mx) * c;
-    const bool need = mx > m_run + kGap;
-    if (__ballot(need)) {
-      const float alpha = need ? fast_exp2(m_run - mx) : 1.f;   // m_run = -inf gives 0
-      if (need) m_run = mx;
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < D / 32; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
-    }
-    const float nm = m_run == -INFINITY ? 0.f : -m_run;
     float pv[32];
+    bool done = false;
+    if (!MASK) {
+      // max-free step on unmasked tiles once every row has a finite running max: p against
+      // the current max; when some lane's sum exceeds kPBound the full step below redoes
+      // the tile's softmax from the same scores
+      if (!__ballot(m_run == -INFINITY)) {
+        const float nm = -m_run;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      pv[e] = fast_exp2(fmaf(s0[e], c, nm));
-      pv[16 + e] = fast_exp2(fmaf(s1[e], c, nm));
+        for (int e = 0; e < 16; ++e) {
+          pv[e] = fast_exp2(fmaf(s0[e], c, nm));
+          pv[16 + e] = fast_exp2(fmaf(s1[e], c, nm));
+        }
+        float ls = 0.f;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) ls += pv[e];
+        if (!__ballot(!(ls <= kPBound))) {
+          l_run += ls;
+          done = true;
+        }
+      }
     }
-    float ls = 0.f;
+    if (!done) {
+      float mx = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 32; ++e) ls += pv[e];
-    l_run += ls;
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fmaxf(s0[e], s1[e]));
+      mx = pair_max(mx) * c;
+      const bool need = mx > m_run + kGap;
+      if (__ballot(need)) {
+        const float alpha = need ? fast_exp2(m_run - mx) : 1.f;   // m_run = -inf gives 0
+        if (need) m_run = mx;
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
+      }
+      const float nm = m_run == -INFINITY ? 0.f : -m_run;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        pv[e] = fast_exp2(fmaf(s0[e], c, nm));
+        pv[16 + e] = fast_exp2(fmaf(s1[e], c, nm));
+      }
+      float ls = 0.f;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) ls += pv[e];
+      l_run += ls;
+    }
     i32x8 pb;
 #pragma unroll
     for (int i = 0; i < 8; ++i) pb[i] = (int)pack_fp8x4(pv[4 * i], pv[4 * i + 1], pv[4 * i + 2], pv[4 * i + 3]);
