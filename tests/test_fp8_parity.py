@@ -21,7 +21,7 @@ import torch
 
 from oracle.attention import attention_fp8_ref, attention_rows, e4m3_value, kv_head_of, visible_keys
 from synth import WORKLOADS
-from synth.fp8 import make_fp8_qkv
+from synth.fp8 import make_fp8_qkv, quantize_heads, v_transposed
 from tests.parity import check_lse, half_spacing_bf16
 
 pytestmark = pytest.mark.gpu
@@ -116,6 +116,35 @@ def test_small_shapes(fa, shape, causal):
     info = _check(o, O, *sens)
     check_lse(lse, L)
     print("  ", info, flush=True)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_late_max_jumps(fa, causal):
+    """Row maxima that jump far above the running max inside the unmasked tiles, where the
+    kernel first tries the max-free step; the lane sums exceed its bound there and the full
+    step reruns on the same scores. Head 0 jumps at keys 700 and 960, head 1 at key 896."""
+    rng = np.random.default_rng(74)
+    B, S, H, d = 1, 1024, 2, 128
+    q = 1.0 + 0.3 * rng.standard_normal((B, S, H, d))       # every row points the same way
+    k = 0.3 * rng.standard_normal((B, S, H, d))
+    v = rng.standard_normal((B, S, H, d))
+    k[0, 700, 0, :] = 3.0                                     # about 49 powers of two up
+    k[0, 960, 0, :] = 6.0                                     # another 49
+    k[0, 896, 1, :] = 6.0
+    q8, qs = quantize_heads(q)
+    k8, ks = quantize_heads(k)
+    v8, vs = quantize_heads(v)
+    vt8, _ = v_transposed(v8)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = _gpu(fa, q8, k8, vt8, qs, ks, vs, causal, scale)
+    O, L = attention_fp8_ref(q8, k8, vt8, qs, ks, vs, causal=causal, scale=scale)
+    Q, K, V = _dequant(q8, k8, vt8, qs, ks, vs, S)
+    sens = [np.zeros((B, S, H, d)) for _ in range(4)]
+    for h in range(H):
+        for x, y in zip(sens, _sensitivities(Q[0, :, h], K[0, :, h], V[0, :, h], np.arange(S), S, causal, scale)):
+            x[0, :, h] = y
+    _check(o, O, *sens)
+    check_lse(lse, L)
 
 
 @pytest.mark.parametrize("scale", [-0.2, 0.0])

@@ -130,6 +130,29 @@ def test_huge_scores_no_overflow(fa):
     assert abs(float(np.median(l - L))) < 1e-2 and l.min() > 10000
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_late_max_jumps(fa, causal):
+    """Row maxima that jump far above the running max deep inside the unmasked tiles, where
+    the kernel forms probabilities without a max reduction and must redo the unit with the
+    full step. Head 0 jumps at key 700 (an odd 32-key unit) and again at key 960 (even
+    unit), head 1 at key 896 (even unit); each jump is over 100 powers of two."""
+    rng = np.random.default_rng(11)
+    B, S, H, d = 1, 1024, 2, 128
+    q = rng.standard_normal((B, S, H, d))
+    k = rng.standard_normal((B, S, H, d))
+    v = rng.standard_normal((B, S, H, d))
+    q[..., 0] = 1.0
+    k[0, 700, 0, 0] = 1024.0          # score about 1024 / sqrt(128): 130 powers of two up
+    k[0, 960, 0, 0] = 3072.0          # a second jump in the same rows
+    k[0, 896, 1, 0] = 2048.0
+    o, l, O, L = _run_full(fa, _bits(q), _bits(k), _bits(v), causal)
+    check_o(o, O, bf16=True)
+    check_lse(l, L)
+    seen = np.arange(S) >= (960 if causal else 0)
+    ref = widen_bf16(_bits(v))[0, 960, 0]
+    assert np.abs(o[0, seen, 0] - ref[None, :]).max() < 1e-2   # the dominant key's V row
+
+
 @pytest.mark.parametrize("scale", [-0.09, 0.0, 0.5])
 def test_other_scales(fa, scale):
     q, k, v = make_qkv(1, 4, 2, 100, 100, 128, seed=9)
