@@ -151,9 +151,13 @@ int fa_decode_combine(const float* part_o, const float* part_lse, void* o, float
  *   seq_lens    : int32 [B]; sequence b holds seq_lens[b] tokens, all visible
  *   o, lse      : bf16 [B, Hq, d] and fp32 [B, Hq] (lse may be NULL)
  *   page_size is a power of two in [16, 2^20]; Hq / Hkv <= 32.
- * Chunks are cut as in fa_decode with Skv = max_blocks_per_seq * page_size
- * (the same chunk length for every sequence); a sequence's chunks past its own
- * length are empty. The merge is fa_decode's. num_splits <= 0 selects the larger
+ * Chunks are cut from the T = ceil(max_blocks_per_seq * page_size / 64) tiles of
+ * 64 keys of the longest possible sequence, the same boundaries for every
+ * sequence: chunk c (0 <= c < n = num_splits) covers tiles
+ * [floor(T c (3n - c) / 2n^2), floor(T (c + 1) (3n - c - 1) / 2n^2)), so chunk
+ * sizes fall from about 1.5 T/n to 0.5 T/n and the grid, which issues every
+ * sequence's first chunk before any second one, runs the largest pieces first.
+ * A sequence's chunks past its own length are empty. The merge is fa_decode's. num_splits <= 0 selects the larger
  * of fa_decode_default_splits(B, Hkv, max_blocks_per_seq * page_size, d) and
  * ceil(max_blocks_per_seq * page_size / 2048) (at most 64). The workspace is
  * fa_decode's: fa_decode_workspace_bytes(B, Hq, d, num_splits) bytes, 256-byte

@@ -103,8 +103,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   // and its chunks past that length are empty.
   int skv = p.Skv;
   if (PAGED) skv = min(max(p.seq_lens[b], 0), p.max_blocks << p.page_log2);
-  const int c0 = cidx * p.chunk;
-  const int c1 = min(skv, c0 + p.chunk);
+  int c0, c1;
+  if (PAGED) {
+    // paged: chunk c covers tiles [T c (3n - c) / 2n^2, ...) of the T tiles of the longest
+    // possible sequence (n = nsplit): sizes fall from about 1.5 T/n to 0.5 T/n, so the
+    // chunk-major grid issues the largest pieces first and the smallest last
+    const long long T = (p.Skv + kSplitAlign - 1) / kSplitAlign, n = p.nsplit, cc = cidx;
+    const long long d2 = 2 * n * n;
+    c0 = kSplitAlign * (int)(T * cc * (3 * n - cc) / d2);
+    c1 = min(skv, kSplitAlign * (int)(T * (cc + 1) * (3 * n - cc - 1) / d2));
+  } else {
+    c0 = cidx * p.chunk;
+    c1 = min(skv, c0 + p.chunk);
+  }
   const int nk = c1 > c0 ? c1 - c0 : 0;
   const int ntiles = (nk + BCT - 1) / BCT;
 
