@@ -361,6 +361,7 @@ int fa_bpt_layer(const void* q, const void* k, const void* v, const void* w1, co
       !aligned16(b2) || !aligned16(y))
     return FA_ERR_ALIGN;
   const int rows_max = block_rows < S ? block_rows : S;
+  if (fa::fwd_grid_size(1, Hq, rows_max) > 0x7fffffffLL) return FA_ERR_SHAPE;
   if (!workspace || workspace_bytes < fa_bpt_workspace_bytes(rows_max, Hq, d, d_ff)) return FA_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return FA_ERR_ALIGN;
   fa::FwdParams p;
