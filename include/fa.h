@@ -257,7 +257,8 @@ size_t fa_bpt_workspace_bytes(int block_rows, int Hq, int d, int d_ff);
  *              256-byte aligned, caller-owned, overwritten.
  * The hidden activations are rounded to bf16 between the two GEMMs (fp32
  * accumulation in each). The GEMMs run on hipBLASLt with the bias and ReLU in its
- * epilogue; the library creates one hipBLASLt handle per process on first use and
+ * epilogue; the library creates one hipBLASLt handle per device (the current device
+ * of the calling thread) on first use, caches the GEMM plans per device and shape, and
  * serialises these calls with a lock. Same shape rules as fa_fwd; d_ff >= 1;
  * block_rows >= 1 (values >= S give the whole-sequence schedule). All tensors are
  * device memory, 16-byte aligned. Launches run on `stream` in order; nothing is
