@@ -13,8 +13,14 @@ import torch
 from . import _lib
 
 
-def _stream_ptr(t: torch.Tensor):
-    return torch.cuda.current_stream(t.device).cuda_stream
+def _launch(ref: torch.Tensor, tensors, fn, *args):
+    """Call library entry point ``fn`` with ``args`` and the current stream of ``ref``'s
+    device, with that device current; every tensor passed must live on it."""
+    for t in tensors:
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"all tensors must be on {ref.device} (got one on {t.device})")
+    with torch.cuda.device(ref.device):
+        return fn(*args, torch.cuda.current_stream(ref.device).cuda_stream)
 
 
 def _need(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int) -> None:
@@ -56,9 +62,10 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
         _need(lse, "lse", torch.float32, 3)
     lib = _lib.load()
     fn = lib.fa_fwd_f32out if out_f32 else lib.fa_fwd
-    st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-            lse.data_ptr() if lse is not None else None,
-            B, Hq, Hkv, Sq, Skv, d, int(bool(causal)), _scale(scale, d), _stream_ptr(q))
+    st = _launch(q, (q, k, v, out, lse), fn,
+                 q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                 lse.data_ptr() if lse is not None else None, B, Hq, Hkv, Sq, Skv, d, int(bool(causal)),
+                 _scale(scale, d))
     _lib.check(st, "fa_fwd_f32out" if out_f32 else "fa_fwd")
     return out, lse
 
@@ -99,10 +106,9 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, scale=
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     _need(out, "out", torch.bfloat16, 3)
     _need(lse, "lse", torch.float32, 2)
-    st = _lib.load().fa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(),
-                               lse.data_ptr(), B, Hq, Hkv, Skv, d, _scale(scale, d), ns,
-                               workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                               _stream_ptr(q))
+    st = _launch(q, (q, k_cache, v_cache, out, lse, workspace), _lib.load().fa_decode,
+                 q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hkv,
+                 Skv, d, _scale(scale, d), ns, workspace.data_ptr(), workspace.numel() * workspace.element_size())
     _lib.check(st, "fa_decode")
     return out, lse
 
@@ -117,9 +123,9 @@ def decode_partials(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
     Skv, Hkv = k_cache.shape[1], k_cache.shape[2]
     part_o = torch.empty((B, Hq, num_splits, d), dtype=torch.float32, device=q.device)
     part_lse = torch.empty((B, Hq, num_splits), dtype=torch.float32, device=q.device)
-    st = _lib.load().fa_decode_partials(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-                                        part_o.data_ptr(), part_lse.data_ptr(), B, Hq, Hkv, Skv, d,
-                                        _scale(scale, d), num_splits, _stream_ptr(q))
+    st = _launch(q, (q, k_cache, v_cache, part_o, part_lse), _lib.load().fa_decode_partials,
+                 q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), part_o.data_ptr(), part_lse.data_ptr(), B,
+                 Hq, Hkv, Skv, d, _scale(scale, d), num_splits)
     _lib.check(st, "fa_decode_partials")
     return part_o, part_lse
 
@@ -133,8 +139,8 @@ def decode_combine(part_o: torch.Tensor, part_lse: torch.Tensor):
         raise ValueError("part_lse shape does not match part_o")
     out = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=part_o.device)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=part_o.device)
-    st = _lib.load().fa_decode_combine(part_o.data_ptr(), part_lse.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                                       B, Hq, d, n, _stream_ptr(part_o))
+    st = _launch(part_o, (part_o, part_lse, out, lse), _lib.load().fa_decode_combine,
+                 part_o.data_ptr(), part_lse.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, d, n)
     _lib.check(st, "fa_decode_combine")
     return out, lse
 
@@ -174,10 +180,11 @@ def decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, 
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     _need(out, "out", torch.bfloat16, 3)
     _need(lse, "lse", torch.float32, 2)
-    st = _lib.load().fa_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), block_table.data_ptr(),
-                                     seq_lens.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, d, page_size,
-                                     max_blocks, num_pages, _scale(scale, d), ns, workspace.data_ptr(),
-                                     workspace.numel() * workspace.element_size(), _stream_ptr(q))
+    st = _launch(q, (q, k_pages, v_pages, block_table, seq_lens, out, lse, workspace), _lib.load().fa_decode_paged,
+                 q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), block_table.data_ptr(),
+                 seq_lens.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, d, page_size, max_blocks,
+                 num_pages, _scale(scale, d), ns, workspace.data_ptr(),
+                 workspace.numel() * workspace.element_size())
     _lib.check(st, "fa_decode_paged")
     return out, lse
 
@@ -212,10 +219,10 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse:
         _need(t, n, torch.bfloat16, 4)
         if tuple(t.shape) != tuple(shp):
             raise ValueError(f"{n} has shape {tuple(t.shape)}, expected {tuple(shp)}")
-    st = _lib.load().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
-                            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Sq, Skv, d,
-                            int(bool(causal)), _scale(scale, d), workspace.data_ptr(),
-                            workspace.numel() * workspace.element_size(), _stream_ptr(q))
+    st = _launch(q, (q, k, v, o, lse, dout, dq, dk, dv, workspace), _lib.load().fa_bwd,
+                 q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                 dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Sq, Skv, d, int(bool(causal)),
+                 _scale(scale, d), workspace.data_ptr(), workspace.numel() * workspace.element_size())
     _lib.check(st, "fa_bwd")
     return dq, dk, dv
 
@@ -250,10 +257,10 @@ def fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, vt8: torch.Tensor, q_scale: torc
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q8.device)
     if lse is not None:
         _need(lse, "lse", torch.float32, 3)
-    st = _lib.load().fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), vt8.data_ptr(), q_scale.data_ptr(),
-                                k_scale.data_ptr(), v_scale.data_ptr(), out.data_ptr(),
-                                lse.data_ptr() if lse is not None else None, B, Hq, Hkv, Sq, Skv, ldv, d,
-                                int(bool(causal)), _scale(scale, d), _stream_ptr(q8))
+    st = _launch(q8, (q8, k8, vt8, q_scale, k_scale, v_scale, out, lse), _lib.load().fa_fwd_fp8,
+                 q8.data_ptr(), k8.data_ptr(), vt8.data_ptr(), q_scale.data_ptr(), k_scale.data_ptr(),
+                 v_scale.data_ptr(), out.data_ptr(), lse.data_ptr() if lse is not None else None, B, Hq, Hkv, Sq,
+                 Skv, ldv, d, int(bool(causal)), _scale(scale, d))
     _lib.check(st, "fa_fwd_fp8")
     return out, lse
 
@@ -292,9 +299,9 @@ def bpt_layer(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w1: torch.Tenso
     if out is None:
         out = torch.empty((B, S, dm), dtype=torch.bfloat16, device=q.device)
     _need(out, "out", torch.bfloat16, 3)
-    st = _lib.load().fa_bpt_layer(q.data_ptr(), k.data_ptr(), v.data_ptr(), w1.data_ptr(), b1.data_ptr(),
-                                  w2.data_ptr(), b2.data_ptr(), out.data_ptr(), B, Hq, Hkv, S, d, d_ff,
-                                  int(bool(causal)), _scale(scale, d), block_rows, workspace.data_ptr(),
-                                  workspace.numel() * workspace.element_size(), _stream_ptr(q))
+    st = _launch(q, (q, k, v, w1, b1, w2, b2, out, workspace), _lib.load().fa_bpt_layer,
+                 q.data_ptr(), k.data_ptr(), v.data_ptr(), w1.data_ptr(), b1.data_ptr(), w2.data_ptr(),
+                 b2.data_ptr(), out.data_ptr(), B, Hq, Hkv, S, d, d_ff, int(bool(causal)), _scale(scale, d),
+                 block_rows, workspace.data_ptr(), workspace.numel() * workspace.element_size())
     _lib.check(st, "fa_bpt_layer")
     return out

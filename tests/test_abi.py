@@ -122,6 +122,18 @@ def test_binding_rejects_cpu_tensors():
         fa.fwd(q, q, q)
 
 
+def test_binding_rejects_mixed_devices():
+    """Every tensor of one call must live on one device; the check runs before any launch."""
+    import torch
+    from io_aware_exact_21_amd import api
+    a = torch.empty(1, device="meta")
+    b = torch.empty(1)
+    called = []
+    with pytest.raises(ValueError, match="all tensors must be on"):
+        api._launch(a, (a, b), lambda *args: called.append(args))
+    assert not called
+
+
 def test_paged_decode_validation(lib):
     from io_aware_exact_21_amd._lib import (FA_ERR_ALIGN, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED,
                                             FA_ERR_WORKSPACE)
