@@ -35,6 +35,7 @@ CASES = [
     (2, 16, 1, 128, 128, [129, 1024], 8),
     (5, 8, 8, 64, 16, [15, 16, 31, 600, 2], 5),
     (1, 32, 1, 128, 256, [700], 2),
+    (2, 8, 2, 128, 16, [40, 7], 16),       # more splits than 64-key tiles: leading chunks empty
     (2, 8, 2, 128, 32, [0, 0], 2),
 ]
 
