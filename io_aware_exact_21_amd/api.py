@@ -79,7 +79,8 @@ def decode_workspace_bytes(B: int, Hq: int, d: int, num_splits: int) -> int:
 
 
 def decode_chunk_bounds(Skv: int, num_splits: int) -> list:
-    """Key ranges of the decode chunks, as the library cuts them (see include/fa.h)."""
+    """Key ranges of the chunks fa_decode / fa_decode_partials cut from a contiguous cache
+    (see include/fa.h; the paged decode cuts chunks of falling size instead)."""
     tiles = (Skv + 63) // 64
     L = 64 * ((tiles + num_splits - 1) // num_splits)
     return [min(Skv, c * L) for c in range(num_splits)] + [Skv]
