@@ -12,8 +12,10 @@
 //     32-key unit it forms S^T = K Q^T and dP^T = V dO^T (a lane owns one query row),
 //     builds dS^T in registers and accumulates dQ^T += K^T dS^T. It also writes D.
 //   * fa_bwd_dkdv_kernel: one workgroup per (batch, KV head, 128 keys). K and V of the
-//     wave's 32 keys stay in registers; Q and dO tiles of every query head of the group
-//     stream through LDS with their LSE and D rows. Per 32-query unit it forms
+//     wave's 32 keys stay in registers; 128-row Q and dO tiles of every query head of the
+//     group stream through a two-stage LDS ring with their LSE and D rows (one barrier per
+//     four 32-query units: with one wave per SIMD every barrier drains the matrix core).
+//     Per 32-query unit it forms
 //     S = Q K^T and dP = dO V^T (a lane owns one key), and accumulates
 //     dV^T += dO^T P and dK^T += Q^T dS.
 // Splitting dQ from dK/dV costs two extra products per tile (S and dP are formed in
@@ -28,8 +30,9 @@ namespace fa {
 
 namespace {
 
-constexpr int kBwdTile = 64;     // rows per streamed LDS tile
-constexpr int kBwdStages = 3;    // LDS ring depth (tiles)
+constexpr int kBwdTile = 64;     // rows per streamed LDS tile (dQ kernel)
+constexpr int kBwdStages = 3;    // LDS ring depth (tiles, dQ kernel)
+constexpr int kBwdDkvTile = 128; // Q / dO rows per dK/dV tile (two-stage ring)
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
@@ -173,11 +176,11 @@ __device__ __forceinline__ void mm_tr_ops(const TrOps<D>& x, u32x4 pb, f32x16 (&
 // Per-lane global byte offsets for the wave-level tile copies: copy n of wave w fills
 // tile rows KPI*(w + NW*n) ...; lane i takes row KPI*(w + NW*n) + i / CPR and fetches
 // global chunk (i % CPR) ^ bswz(row), so LDS chunk c of the row holds chunk c ^ bswz.
-template <int D, int NW>
+template <int D, int NW, int BT = kBwdTile>
 struct TileDma {
   static constexpr int CPR = D / 8;
   static constexpr int KPI = 64 / CPR;
-  static constexpr int NI = kBwdTile / KPI;
+  static constexpr int NI = BT / KPI;
   static constexpr int NPW = NI / NW;            // copies per wave and tensor
   static_assert(NI % NW == 0, "copies must split evenly over the waves");
   unsigned off[NPW];
@@ -197,7 +200,7 @@ struct TileDma {
   __device__ __forceinline__ void copy(const uint16_t* base, int64_t row_stride, int r0, int rmax, unsigned dst,
                                        int w, int lane) const {
     const uint16_t* t = base + (int64_t)r0 * row_stride;
-    if (r0 + kBwdTile <= rmax) {
+    if (r0 + BT <= rmax) {
 #pragma unroll
       for (int n = 0; n < NPW; ++n) dma16(t, off[n], dst + (w + NW * n) * 1024);
     } else {
@@ -357,12 +360,12 @@ void fa_bwd_dq_kernel(BwdParams p) {
 // of the KV head's group.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwdDkvWaves * 64) void fa_bwd_dkdv_kernel(BwdParams p) {
-  constexpr int NW = kBwdDkvWaves, BT = kBwdTile, NS = kBwdStages, BC = kBwdDkvKeys;
+  constexpr int NW = kBwdDkvWaves, BT = kBwdDkvTile, NS = 2, BC = kBwdDkvKeys;
   constexpr unsigned TB = BT * D * 2;                    // bytes per Q / dO tile
   constexpr unsigned VB = BT * 4;                        // bytes per LSE / D tile
   // Q stages, dO stages, LSE stages, D stages
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * NS * TB + 2 * NS * VB];
-  static_assert(NW % 2 == 0, "waves alternate between the LSE and D copies");
+  static_assert(NW == 4, "waves 0..3 copy LSE and D, 64 rows each");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -410,10 +413,8 @@ __global__ __launch_bounds__(kBwdDkvWaves * 64) void fa_bwd_dkdv_kernel(BwdParam
   const unsigned lse_ring = ring + 2 * NS * TB;
   const unsigned dsum_ring = lse_ring + NS * VB;
   const int64_t q_stride = (int64_t)p.Hq * D;
-  TileDma<D, NW> dma;
+  TileDma<D, NW, BT> dma;
   dma.init(q_stride, w, lane);
-  constexpr int PER_IT = 2 * TileDma<D, NW>::NPW + 1;   // copies per wave and iteration
-  const unsigned row_off = (unsigned)lane * 4u;
 
   auto issue = [&](int it) {
     const int hq = hk * grp + it / nqt;
@@ -422,11 +423,13 @@ __global__ __launch_bounds__(kBwdDkvWaves * 64) void fa_bwd_dkdv_kernel(BwdParam
     const int64_t hoff = ((int64_t)b * p.Sq * p.Hq + hq) * D;
     dma.copy(p.q + hoff, q_stride, r0, p.Sq, ring + st * TB, w, lane);
     dma.copy(p.dout + hoff, q_stride, r0, p.Sq, ring + (NS + st) * TB, w, lane);
-    // LSE and D rows of the tile (rows past Sq re-read row Sq - 1)
+    // LSE (even waves) and D (odd waves) rows of the tile, 64 rows per wave; rows past Sq
+    // re-read row Sq - 1 (r0 < Sq, so the offset is never negative)
     const int64_t soff = ((int64_t)b * p.Hq + hq) * p.Sq + r0;
-    const unsigned ro = (unsigned)min(lane, p.Sq - 1 - r0) * 4u;
-    if ((w & 1) == 0) dma4(p.lse + soff, r0 + 64 <= p.Sq ? row_off : ro, lse_ring + st * VB);
-    else dma4(p.dsum + soff, r0 + 64 <= p.Sq ? row_off : ro, dsum_ring + st * VB);
+    const int half = w >> 1;
+    const unsigned ro = (unsigned)min(64 * half + lane, p.Sq - 1 - r0) * 4u;
+    if ((w & 1) == 0) dma4(p.lse + soff, ro, lse_ring + st * VB + 256u * half);
+    else dma4(p.dsum + soff, ro, dsum_ring + st * VB + 256u * half);
   };
 
   f32x16 dk[D / 32], dv[D / 32];
@@ -437,22 +440,20 @@ __global__ __launch_bounds__(kBwdDkvWaves * 64) void fa_bwd_dkdv_kernel(BwdParam
   }
 
   if (n_it > 0) issue(0);
-  if (n_it > 1) issue(1);
   for (int it = 0; it < n_it; ++it) {
-    if (it + 1 < n_it) wait_vmcnt<PER_IT>();
-    else wait_vmcnt<0>();
-    __syncthreads();
-    if (it + 2 < n_it) issue(it + 2);
+    wait_vmcnt<0>();                                     // tile it landed (the only copies in flight)
+    __syncthreads();                                     // every wave's share landed; tile it - 1 is free
+    if (it + 1 < n_it) issue(it + 1);
     const unsigned st = (unsigned)(it % NS);
     const unsigned qst = ring + st * TB, dst = ring + (NS + st) * TB;
     const unsigned lst = lse_ring + st * VB, sst = dsum_ring + st * VB;
     const int r0 = (qt0 + it % nqt) * BT;
     // One code path for every tile (no branch around the accumulator updates, so the
     // accumulators stay in place across iterations); masks are applied in place. The
-    // two units run one after the other: unrolled, their operand prefetches together
-    // exceed the 256 architected VGPRs and the overflow costs more than it hides.
+    // four units run one after the other: prefetching the next unit's operands under the
+    // current unit's products overflows the architected VGPRs and gains nothing.
 #pragma unroll 1
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < BT / 32; ++u) {
       const int qu0 = r0 + 32 * u;                       // first query row of the unit
       const RowOps<D> aq = load_rows<D>(qst + u * 32 * D * 2, g);
       const RowOps<D> ad = load_rows<D>(dst + u * 32 * D * 2, g);
