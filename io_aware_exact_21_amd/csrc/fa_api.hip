@@ -56,7 +56,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
   p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Sq = Sq; p.Skv = Skv; p.d = d;
   st = scale_terms(scale, &p.c, &p.qsign, &p.qmask);
   if (st != FA_OK) return st;
-  if (fa::fwd_grid_size(B, Hq, Sq) > 0x7fffffffLL) return FA_ERR_SHAPE;
+  if (fa::fwd_grid_size(B, Hq, Sq, d) > 0x7fffffffLL) return FA_ERR_SHAPE;
   (void)hipGetLastError();
   if (fa::launch_fwd(p, causal != 0, out_f32, static_cast<hipStream_t>(stream)) != hipSuccess) return FA_ERR_HIP;
   return FA_OK;
@@ -361,7 +361,7 @@ int fa_bpt_layer(const void* q, const void* k, const void* v, const void* w1, co
       !aligned16(b2) || !aligned16(y))
     return FA_ERR_ALIGN;
   const int rows_max = block_rows < S ? block_rows : S;
-  if (fa::fwd_grid_size(1, Hq, rows_max) > 0x7fffffffLL) return FA_ERR_SHAPE;
+  if (fa::fwd_grid_size(1, Hq, rows_max, d) > 0x7fffffffLL) return FA_ERR_SHAPE;
   if (!workspace || workspace_bytes < fa_bpt_workspace_bytes(rows_max, Hq, d, d_ff)) return FA_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return FA_ERR_ALIGN;
   fa::FwdParams p;

@@ -1,7 +1,8 @@
 // Fused exact attention forward for gfx950.
 //
-// One workgroup of eight waves (two per SIMD) owns BR = 256 query rows of one
-// (batch, query head); each wave owns 32 of them, the 32 columns of its MFMA tiles.
+// One workgroup of eight waves (two per SIMD; four waves at d = 64, two workgroups per
+// CU) owns BR = 256 (128) query rows of one (batch, query head); each wave owns 32 of
+// them, the 32 columns of its MFMA tiles.
 // The Q rows stay in registers for the whole kernel while K/V tiles of 64 keys
 // stream through a three-stage LDS ring filled by direct global->LDS loads
 // ("I/O-Aware Kernels", section FlashAttention: Q blocks resident, K and V streamed
@@ -363,8 +364,8 @@ struct FwdWave {
 }  // namespace
 
 template <int D, bool CAUSAL, bool OUT_F32>
-__global__ __launch_bounds__(kFwdWaves * 64) void fa_fwd_kernel(FwdParams p) {
-  constexpr int NW = kFwdWaves;
+__global__ __launch_bounds__(fwd_waves(D) * 64, 2) void fa_fwd_kernel(FwdParams p) {
+  constexpr int NW = fwd_waves(D);
   constexpr int BCT = kFwdTile;
   constexpr int NS = kFwdStages;
   constexpr int BR = 32 * NW;
@@ -533,14 +534,14 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fa_fwd_kernel(FwdParams p) {
 
 template <int D, bool CAUSAL, bool OUT_F32>
 static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream) {
-  const long long total = fwd_grid_size(p.B, p.Hq, p.Sq);
-  hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, OUT_F32>), dim3((unsigned)total), dim3(kFwdWaves * 64), 0,
+  const long long total = fwd_grid_size(p.B, p.Hq, p.Sq, D);
+  hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, OUT_F32>), dim3((unsigned)total), dim3(fwd_waves(D) * 64), 0,
                      stream, p);
   return hipGetLastError();
 }
 
-long long fwd_grid_size(int B, int Hq, int Sq) {
-  constexpr int BR = 32 * kFwdWaves;
+long long fwd_grid_size(int B, int Hq, int Sq, int d) {
+  const int BR = 32 * fwd_waves(d);
   return (long long)B * Hq * ((Sq + BR - 1) / BR);
 }
 

@@ -9,6 +9,9 @@ namespace fa {
 // Waves per prefill workgroup (32 query rows each, two waves per SIMD) and per
 // decode-split workgroup (each wave takes 32 keys of every KV tile).
 constexpr int kFwdWaves = 8;
+// At d = 64 a prefill workgroup has four waves (128 query rows) and two workgroups
+// share a CU: the finer grain shortens the causal tail of the small-head shapes.
+constexpr int fwd_waves(int d) { return d == 64 ? 4 : kFwdWaves; }
 constexpr int kDecWaves = 2;
 constexpr int kDecTile = 32 * kDecWaves;   // keys per decode KV tile
 constexpr int kSplitAlign = 64;            // decode chunk lengths are multiples of this
@@ -53,7 +56,7 @@ struct CombineParams {
   int d, nsplit;
 };
 
-long long fwd_grid_size(int B, int Hq, int Sq);
+long long fwd_grid_size(int B, int Hq, int Sq, int d);
 hipError_t launch_fwd(const FwdParams& p, bool causal, bool out_f32, hipStream_t stream);
 hipError_t launch_decode_partials(const DecParams& p, hipStream_t stream);
 hipError_t launch_decode_paged_partials(const DecParams& p, hipStream_t stream);
