@@ -326,7 +326,7 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* vt8, const float* q_s
   if ((reinterpret_cast<uintptr_t>(q_scale) | reinterpret_cast<uintptr_t>(k_scale) |
        reinterpret_cast<uintptr_t>(v_scale)) & 3u)
     return FA_ERR_ALIGN;
-  if (fa::fp8_grid_size(B, Hq, Sq) > 0x7fffffffLL) return FA_ERR_SHAPE;
+  if (fa::fp8_grid_size(B, Hq, Sq, d) > 0x7fffffffLL) return FA_ERR_SHAPE;
   fa::Fp8Params p;
   p.q = static_cast<const uint8_t*>(q8);
   p.k = static_cast<const uint8_t*>(k8);

@@ -7,7 +7,10 @@
 namespace fa {
 
 constexpr int kFp8Waves = 8;                 // 32 query rows per wave
-constexpr int kFp8Rows = 32 * kFp8Waves;     // query rows per workgroup
+// At d = 64 a workgroup has four waves (128 query rows) and two workgroups share a CU:
+// the finer grain shortens the causal tail of the small-head shapes.
+constexpr int fp8_waves(int d) { return d == 64 ? 4 : kFp8Waves; }
+constexpr int fp8_rows(int d) { return 32 * fp8_waves(d); }   // query rows per workgroup
 
 struct Fp8Params {
   const uint8_t* q;        // [B, Sq, Hq, d]   e4m3 codes
@@ -22,7 +25,7 @@ struct Fp8Params {
   float c;                 // softmax scale * log2(e) (any sign); the per-head scales multiply in
 };
 
-long long fp8_grid_size(int B, int Hq, int Sq);
+long long fp8_grid_size(int B, int Hq, int Sq, int d);
 hipError_t launch_fwd_fp8(const Fp8Params& p, bool causal, hipStream_t stream);
 
 }  // namespace fa

@@ -144,8 +144,8 @@ __device__ __forceinline__ unsigned pack_fp8x4(float a, float b, float c, float 
 }  // namespace
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kFp8Waves * 64) void fa_fwd_fp8_kernel(Fp8Params p) {
-  constexpr int NW = kFp8Waves, BR = kFp8Rows;
+__global__ __launch_bounds__(fp8_waves(D) * 64, 2) void fa_fwd_fp8_kernel(Fp8Params p) {
+  constexpr int NW = fp8_waves(D), BR = fp8_rows(D);
   using R = Ring<D>;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[R::kBytes];
 
@@ -361,10 +361,12 @@ __global__ __launch_bounds__(kFp8Waves * 64) void fa_fwd_fp8_kernel(Fp8Params p)
   }
 }
 
-long long fp8_grid_size(int B, int Hq, int Sq) { return (long long)B * Hq * ((Sq + kFp8Rows - 1) / kFp8Rows); }
+long long fp8_grid_size(int B, int Hq, int Sq, int d) {
+  return (long long)B * Hq * ((Sq + fp8_rows(d) - 1) / fp8_rows(d));
+}
 
 hipError_t launch_fwd_fp8(const Fp8Params& p, bool causal, hipStream_t stream) {
-  const dim3 grid((unsigned)fp8_grid_size(p.B, p.Hq, p.Sq)), block(kFp8Waves * 64);
+  const dim3 grid((unsigned)fp8_grid_size(p.B, p.Hq, p.Sq, p.d)), block(fp8_waves(p.d) * 64);
   if (p.d == 128) {
     if (causal) hipLaunchKernelGGL((fa_fwd_fp8_kernel<128, true>), grid, block, 0, stream, p);
     else hipLaunchKernelGGL((fa_fwd_fp8_kernel<128, false>), grid, block, 0, stream, p);
