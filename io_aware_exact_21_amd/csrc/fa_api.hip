@@ -289,7 +289,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
     return FA_ERR_ALIGN;
   if (!workspace || workspace_bytes < fa_bwd_workspace_bytes(B, Hq, Sq)) return FA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return FA_ERR_ALIGN;
-  if (fa::bwd_dq_grid(B, Hq, Sq) > 0x7fffffffLL || fa::bwd_dkdv_grid(B, Hkv, Skv) > 0x7fffffffLL) return FA_ERR_SHAPE;
+  if (fa::bwd_dq_grid(B, Hq, Sq, d) > 0x7fffffffLL || fa::bwd_dkdv_grid(B, Hkv, Skv) > 0x7fffffffLL) return FA_ERR_SHAPE;
   fa::BwdParams p;
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);

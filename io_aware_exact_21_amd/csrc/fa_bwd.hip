@@ -7,8 +7,9 @@
 //     dV_j = sum_i P_ij dO_i,   dK_j = scale sum_i dS_ij Q_i,   dQ_i = scale sum_j dS_ij K_j.
 //
 // Two kernels, neither with atomics:
-//   * fa_bwd_dq_kernel: one workgroup per (batch, query head, 256 query rows). Q and dO
-//     of the wave's 32 rows stay in registers; K and V tiles stream through LDS. Per
+//   * fa_bwd_dq_kernel: one workgroup per (batch, query head, 256 query rows; 128 at
+//     d = 64). Q and dO of the wave's 32 rows stay in registers; K and V tiles stream
+//     through LDS. Per
 //     32-key unit it forms S^T = K Q^T and dP^T = V dO^T (a lane owns one query row),
 //     builds dS^T in registers and accumulates dQ^T += K^T dS^T. It also writes D.
 //   * fa_bwd_dkdv_kernel: one workgroup per (batch, KV head, 128 keys). K and V of the
@@ -226,11 +227,11 @@ __device__ __forceinline__ void store4(uint16_t* dst, const f32x16& a, int i, fl
 }  // namespace
 
 // ---------------------------------------------------------------------------------------
-// dQ (and D): one workgroup per (batch, query head, kBwdDqRows query rows).
+// dQ (and D): one workgroup per (batch, query head, bwd_dq_rows(D) query rows).
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdDqWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(bwd_dq_waves(D) * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void fa_bwd_dq_kernel(BwdParams p) {
-  constexpr int NW = kBwdDqWaves, BT = kBwdTile, NS = kBwdStages, BR = kBwdDqRows;
+  constexpr int NW = bwd_dq_waves(D), BT = kBwdTile, NS = kBwdStages, BR = bwd_dq_rows(D);
   constexpr unsigned TB = BT * D * 2;                    // bytes per tile
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * NS * TB];   // K stages, then V stages
 
@@ -510,15 +511,17 @@ __global__ __launch_bounds__(kBwdDkvWaves * 64) void fa_bwd_dkdv_kernel(BwdParam
   }
 }
 
-long long bwd_dq_grid(int B, int Hq, int Sq) { return (long long)B * Hq * ((Sq + kBwdDqRows - 1) / kBwdDqRows); }
+long long bwd_dq_grid(int B, int Hq, int Sq, int d) {
+  return (long long)B * Hq * ((Sq + bwd_dq_rows(d) - 1) / bwd_dq_rows(d));
+}
 long long bwd_dkdv_grid(int B, int Hkv, int Skv) {
   return (long long)B * Hkv * ((Skv + kBwdDkvKeys - 1) / kBwdDkvKeys);
 }
 
 template <int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)bwd_dq_grid(p.B, p.Hq, p.Sq)),
-                     dim3(kBwdDqWaves * 64), 0, stream, p);
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)bwd_dq_grid(p.B, p.Hq, p.Sq, D)),
+                     dim3(bwd_dq_waves(D) * 64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)bwd_dkdv_grid(p.B, p.Hkv, p.Skv)),

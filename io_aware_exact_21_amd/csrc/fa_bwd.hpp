@@ -11,7 +11,10 @@ namespace fa {
 // accumulators alone take 128 registers per lane).
 constexpr int kBwdDqWaves = 8;
 constexpr int kBwdDkvWaves = 4;
-constexpr int kBwdDqRows = 32 * kBwdDqWaves;    // query rows per dQ workgroup
+// At d = 64 a dQ workgroup has four waves (128 query rows) and two share a CU: the finer
+// grain shortens the causal tail of the small-head shapes.
+constexpr int bwd_dq_waves(int d) { return d == 64 ? 4 : kBwdDqWaves; }
+constexpr int bwd_dq_rows(int d) { return 32 * bwd_dq_waves(d); }   // query rows per dQ workgroup
 constexpr int kBwdDkvKeys = 32 * kBwdDkvWaves;  // keys per dK/dV workgroup
 
 struct BwdParams {
@@ -30,7 +33,7 @@ struct BwdParams {
   float scale;
 };
 
-long long bwd_dq_grid(int B, int Hq, int Sq);
+long long bwd_dq_grid(int B, int Hq, int Sq, int d);
 long long bwd_dkdv_grid(int B, int Hkv, int Skv);
 // dQ kernel (which also writes dsum), then dK/dV kernel, on one stream.
 hipError_t launch_bwd(const BwdParams& p, bool causal, hipStream_t stream);
