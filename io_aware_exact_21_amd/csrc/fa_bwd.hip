@@ -9,9 +9,9 @@
 // Two kernels, neither with atomics:
 //   * fa_bwd_dq_kernel: one workgroup per (batch, query head, 256 query rows; 128 at
 //     d = 64). Q and dO of the wave's 32 rows stay in registers; K and V tiles stream
-//     through LDS. Per
-//     32-key unit it forms S^T = K Q^T and dP^T = V dO^T (a lane owns one query row),
-//     builds dS^T in registers and accumulates dQ^T += K^T dS^T. It also writes D.
+//     through LDS. Per 32-key unit it forms S^T = K Q^T and dP^T = V dO^T (a lane owns
+//     one query row), builds dS^T in registers and accumulates dQ^T += K^T dS^T. It also
+//     writes D.
 //   * fa_bwd_dkdv_kernel: one workgroup per (batch, KV head, 128 keys). K and V of the
 //     wave's 32 keys stay in registers; 128-row Q and dO tiles of every query head of the
 //     group stream through a two-stage LDS ring with their LSE and D rows (one barrier per
