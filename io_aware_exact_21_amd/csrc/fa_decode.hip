@@ -51,8 +51,8 @@ struct PagedTileCopy : TileCopy<D, BCT, NT> {
     for (int p = 0; p < PER_T; ++p) {
       u32x4 zk = {0u, 0u, 0u, 0u}, zv = {0u, 0u, 0u, 0u};
       if (key0 + p < kmax) {
-        zk = *reinterpret_cast<const u32x4*>(kp + base + p * row_stride);
-        zv = *reinterpret_cast<const u32x4*>(vp + base + p * row_stride);
+        zk = stream_load16(kp + base + p * row_stride);
+        zv = stream_load16(vp + base + p * row_stride);
       }
       this->kr[p] = zk;
       this->vr[p] = zv;
