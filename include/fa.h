@@ -95,7 +95,9 @@ int fa_fwd_f32out(const void* q, const void* k, const void* v, float* o, float* 
  * (an empty chunk has lambda_c = -inf and weight 0).
  */
 
-/* Heuristic split count used when num_splits <= 0 (always >= 1). */
+/* Heuristic split count used when num_splits <= 0 (always >= 1): about two
+ * workgroups (one per (sequence, KV head, chunk)) per compute unit, chunks of at
+ * least 512 keys, at most 64 chunks. */
 int fa_decode_default_splits(int B, int Hkv, int Skv, int d);
 
 /* Bytes of workspace fa_decode needs for this shape and split count

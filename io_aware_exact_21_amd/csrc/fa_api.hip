@@ -174,10 +174,11 @@ int fa_fwd_f32out(const void* q, const void* k, const void* v, float* o, float* 
 int fa_decode_default_splits(int B, int Hkv, int Skv, int d) {
   (void)d;
   if (B < 1 || Hkv < 1 || Skv < 1) return 1;
-  // Aim for about four workgroups per compute unit (256 CUs) while keeping every
-  // chunk at least 512 keys long.
+  // Aim for about two workgroups per compute unit (256 CUs) while keeping every chunk
+  // at least 512 keys long: with non-temporal cache loads, 512 workgroups of long chunks
+  // stream HBM faster than more, shorter ones (B 4..64, Hkv 8, Skv 4096..16384, d 128).
   const long long units = (long long)B * Hkv;
-  long long want = (4LL * 256 + units - 1) / units;
+  long long want = (2LL * 256 + units - 1) / units;
   long long most = (Skv + 511) / 512;
   if (want > most) want = most;
   if (want > 64) want = 64;
