@@ -3,7 +3,8 @@
 One step = one pass of the whole hot path on resident synthetic inputs:
   fa_fwd on the long-prefill workload (B2 H32 S8192 d128, causal, K x4 on 1% of positions),
   then the split-KV decode (B64 Hq32 Hkv8 Skv16384 d128): chunk partials + log-sum-exp merge.
-W untimed warmup steps, then K timed steps between device synchronisations. Every kernel
+W untimed warmup steps (default 50), then K timed steps (default 100) between device
+synchronisations. Every kernel
 is bracketed by HIP events recorded on the stream the library launches on (torch's
 current stream, which is passed to the library), giving per-kernel average durations.
 
@@ -305,8 +306,10 @@ def bpt_bench(fa, stream, w, tq, tk, tv, steps: int, warmup: int, block_rows: in
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # The compute-bound kernels reach their sustained clock only after some tens of
+    # milliseconds of load: 50 warm-up steps (about 0.1 s) precede the 100 timed ones.
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--fwd-workload", default="mha8k", choices=["tiny", "mha2k", "mha8k", "gqa32k"])
     # The decode workload splits the KV length into chunks and merges them by log-sum-exp,
     # so the bench runs two chunks per sequence; at this batch (B 64, Hkv 8) the library's

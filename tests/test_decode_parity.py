@@ -102,18 +102,24 @@ def test_decode_deterministic(fa):
 
 
 def test_decode_workload_sampled(fa):
-    """The full decode workload at the benchmark's default split count; the oracle computes
-    sampled (sequence, head) rows one by one; the whole output is checked for finiteness."""
+    """The full decode workload with the two KV chunks the benchmark times and with the
+    library's default split count; the oracle computes sampled (sequence, head) rows one by
+    one; the whole output is checked for finiteness."""
     w = WORKLOADS["decode"]
     print("decode workload: generating inputs", flush=True)
     q, k, v = make_workload(w)
     tq, tk, tv = up(q), up(k), up(v)
-    o, lse = fa.decode(tq, tk, tv, scale=w.scale)
-    torch.cuda.synchronize()
-    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
     rng = np.random.default_rng(w.seed)
-    o_np, l_np = down(o), down(lse)
-    for b in sorted(set([0, w.B - 1] + [int(x) for x in rng.integers(0, w.B, 4)])):
-        O, L = decode_ref(widen_bf16(q[b:b + 1]), widen_bf16(k[b:b + 1]), widen_bf16(v[b:b + 1]), scale=w.scale)
-        check_o(o_np[b:b + 1], O, bf16=True, what=f"O[{b}]")
-        check_lse(l_np[b:b + 1], L, what=f"LSE[{b}]")
+    batches = sorted(set([0, w.B - 1] + [int(x) for x in rng.integers(0, w.B, 4)]))
+    refs = {b: decode_ref(widen_bf16(q[b:b + 1]), widen_bf16(k[b:b + 1]), widen_bf16(v[b:b + 1]), scale=w.scale)
+            for b in batches}
+    for ns in (2, 0):
+        print(f"decode workload: num_splits {ns}", flush=True)
+        o, lse = fa.decode(tq, tk, tv, scale=w.scale, num_splits=ns)
+        torch.cuda.synchronize()
+        assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+        o_np, l_np = down(o), down(lse)
+        for b in batches:
+            O, L = refs[b]
+            check_o(o_np[b:b + 1], O, bf16=True, what=f"O[{b}] (num_splits {ns})")
+            check_lse(l_np[b:b + 1], L, what=f"LSE[{b}] (num_splits {ns})")
