@@ -51,10 +51,11 @@ def test_small_shapes(fa, shape, causal):
     check_lse(l, L)
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("causal", [False, True])
-def test_fp32_output_arithmetic(fa, causal):
+def test_fp32_output_arithmetic(fa, causal, d):
     """fp32-output instantiation: the kernel arithmetic meets 1e-2 / 4e-3 with no output rounding."""
-    q, k, v = make_qkv(2, 8, 2, 300, 300, 128, seed=31)
+    q, k, v = make_qkv(2, 8, 2, 300, 300, d, seed=31)
     o, l, O, L = _run_full(fa, q, k, v, causal, out_f32=True)
     info = check_o(o, O, bf16=False)
     assert info["max_abs"] < 5e-3
