@@ -156,6 +156,25 @@ __device__ __forceinline__ void pv_unit(const unsigned (&va)[D / 32], unsigned i
   }
 }
 
+// Order of the steps of a hot-loop slot: position p runs step at[p] (steps below NQK are
+// Q.K^T, the rest P.V). Two Q.K^T steps open the slot, then P.V and Q.K^T alternate until
+// the Q.K^T steps run out, so the K and V operand reads spread evenly over the slot and
+// the scores' dependent chain still ends a few steps before the slot does.
+template <int NQK, int NPV>
+struct SlotOrder {
+  int at[NQK + NPV];
+  constexpr SlotOrder() : at() {
+    int q = 0, v = 0, p = 0;
+    at[p++] = q++;
+    at[p++] = q++;
+    while (q < NQK) {
+      at[p++] = NQK + v++;
+      at[p++] = q++;
+    }
+    while (v < NPV) at[p++] = NQK + v++;
+  }
+};
+
 __device__ __forceinline__ unsigned bf16_pair_sum_weights() { return 0x3F803F80u; }   // (1.0, 1.0)
 
 // Online-softmax step of one 32-row group over one 32-key unit. `s` holds this lane's
@@ -257,17 +276,19 @@ struct FwdWave {
     u32x4 op[N];
     float pe[16];
     unsigned pk[8];
-    // steps [0, NQK): Q.K^T; steps [NQK, N): P.V
-    auto load = [&](int i) {
+    // steps [0, NQK): Q.K^T; steps [NQK, N): P.V; position i runs step ord.at[i]
+    constexpr SlotOrder<NQK, NPV> ord;
+    auto load = [&](int pos) {
+      const int i = ord.at[pos];
       if (i >= NQK) {
         const int tt = (i - NQK) / NDB, db = (i - NQK) % NDB;
         const lds_u8* a0p = lds_ptr(va[db]) + imm + tt * 16 * D * 2;
         const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0p));
         const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0p + 8 * D * 2));
         const u32x2 x0 = __builtin_bit_cast(u32x2, r0), x1 = __builtin_bit_cast(u32x2, r1);
-        op[i] = u32x4{x0[0], x0[1], x1[0], x1[1]};
+        op[pos] = u32x4{x0[0], x0[1], x1[0], x1[1]};
       } else {
-        op[i] = *reinterpret_cast<const lds_u32x4*>(lds_ptr(ka[i]) + imm);
+        op[pos] = *reinterpret_cast<const lds_u32x4*>(lds_ptr(ka[i]) + imm);
       }
     };
     load(0);
@@ -277,11 +298,12 @@ struct FwdWave {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       if (i + 2 < N) load(i + 2);
-      if (i >= NQK) {
-        const int tt = (i - NQK) / NDB, db = (i - NQK) % NDB;
+      const int st = ord.at[i];
+      if (st >= NQK) {
+        const int tt = (st - NQK) / NDB, db = (st - NQK) % NDB;
         o[db] = mfma_32x32x16(op[i], pin[tt], o[db]);
       } else {
-        s = mfma_32x32x16(op[i], q[i], s);
+        s = mfma_32x32x16(op[i], q[st], s);
       }
 #pragma unroll
       for (int e = E * i; e < E * i + E; ++e) {
