@@ -325,8 +325,8 @@ def main() -> int:
                     help="only run plain device copies of MIB MiB (reference reading for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
-              "(the kernels shard by independent heads or KV chunks with no exchange; see the design notes)",
+        print(f"bench.py: runs on one GPU only; --gpus {args.gpus} is not supported (the prefill and "
+              "decode kernels shard by independent heads or KV chunks, one share per GPU, with no exchange)",
               file=sys.stderr)
         return 2
 
