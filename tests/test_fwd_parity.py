@@ -51,6 +51,25 @@ def test_small_shapes(fa, shape, causal):
     check_lse(l, L)
 
 
+# More query tiles than the chip has CUs: the forward then runs on its persistent grid, so
+# these cover the hand-over from one work unit to the next (ragged tiles, GQA, Sq != Skv).
+MANY_UNITS = [
+    # B, Hq, Hkv, Sq, Skv, d
+    (3, 40, 8, 700, 700, 128), (2, 48, 16, 600, 900, 128), (3, 40, 8, 700, 700, 64), (1, 96, 96, 333, 333, 64),
+]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", MANY_UNITS, ids=[str(s) for s in MANY_UNITS])
+def test_many_work_units(fa, shape, causal):
+    B, Hq, Hkv, Sq, Skv, d = shape
+    q, k, v = make_qkv(B, Hq, Hkv, Sq, Skv, d, seed=300 + Sq + Skv + d)
+    print(f"case {shape} causal={causal}", flush=True)
+    o, l, O, L = _run_full(fa, q, k, v, causal)
+    check_o(o, O, bf16=True)
+    check_lse(l, L)
+
+
 @pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("causal", [False, True])
 def test_fp32_output_arithmetic(fa, causal, d):
