@@ -74,6 +74,21 @@ def measured_traffic(name: str, family: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def measured_mfma_util(name: str, family: str):
+    """Matrix-core utilisation and shader clock from the committed counter summary, if taken
+    on the current kernel sources."""
+    path = os.path.join(PROFILES, name)
+    try:
+        with open(path) as f:
+            rec = json.loads(next(l for l in f if l.startswith("{")))
+    except (OSError, StopIteration, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash(family):
+        return None
+    return {"mfma_util": rec.get("mfma_util"), "shader_clock_ghz": rec.get("shader_clock_ghz"),
+            "source": "rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs), sustained dispatches"}
+
+
 def cpu_baseline(w, q, k, v, budget_s: float) -> dict:
     """The fp64 oracle, as it stands, on whole heads of the same workload until the budget is used."""
     import numpy as np
@@ -424,7 +439,9 @@ def main() -> int:
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_BF16_TFLOPS, 4), "traffic": t_fwd,
                      "kernel": "fa_fwd_kernel", "avg_kernel_ms": round(fwd_ms, 4),
-                     "algorithmic_flops": flops, "algorithmic_bytes": fwd_bytes(wf)},
+                     "algorithmic_flops": flops, "algorithmic_bytes": fwd_bytes(wf),
+                     "counters": measured_mfma_util("mfma_utilisation_counters.txt", "fwd")
+                     if args.fwd_workload == "mha8k" else None},
         "decode": {
             "config": {**wd.describe(), "num_splits": ns, "seed": wd.seed},
             "value": round(dec_gbs, 1), "unit": "GB/s", "ms": round(split_ms + comb_ms, 4),
