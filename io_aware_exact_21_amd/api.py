@@ -15,23 +15,29 @@ from . import _lib
 
 def _launch(ref: torch.Tensor, tensors, fn, *args):
     """Call library entry point ``fn`` with ``args`` and the current stream of ``ref``'s
-    device, with that device current; every tensor passed must live on it."""
+    device, with that device current; ``ref`` must be a GPU tensor and every tensor
+    passed must live on its device."""
     for t in tensors:
         if t is not None and t.device != ref.device:
             raise ValueError(f"all tensors must be on {ref.device} (got one on {t.device})")
+    if ref.device.type != "cuda":
+        raise ValueError(f"tensors must be GPU tensors (got {ref.device}); there is no CPU path")
     with torch.cuda.device(ref.device):
         return fn(*args, torch.cuda.current_stream(ref.device).cuda_stream)
 
 
-def _need(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int) -> None:
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int, shape=None) -> None:
+    """Check a tensor argument's type, dtype, rank and contiguity; with ``shape`` its exact
+    shape too (every output is checked this way, so an undersized caller-supplied buffer
+    is rejected before any launch). Devices are checked by ``_launch``."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
-        raise ValueError(f"{name} must be a GPU tensor (got {t.device}); there is no CPU path")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
     if t.dim() != ndim or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous {ndim}-d tensor (got shape {tuple(t.shape)})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
 def _scale(scale, d: int) -> float:
@@ -55,11 +61,11 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
     odt = torch.float32 if out_f32 else torch.bfloat16
     if out is None:
         out = torch.empty((B, Sq, Hq, d), dtype=odt, device=q.device)
-    _need(out, "out", odt, 4)
+    _need(out, "out", odt, 4, (B, Sq, Hq, d))
     if return_lse and lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
     if lse is not None:
-        _need(lse, "lse", torch.float32, 3)
+        _need(lse, "lse", torch.float32, 3, (B, Hq, Sq))
     lib = _lib.load()
     fn = lib.fa_fwd_f32out if out_f32 else lib.fa_fwd
     st = _launch(q, (q, k, v, out, lse), fn,
@@ -105,8 +111,8 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, scale=
         out = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    _need(out, "out", torch.bfloat16, 3)
-    _need(lse, "lse", torch.float32, 2)
+    _need(out, "out", torch.bfloat16, 3, (B, Hq, d))
+    _need(lse, "lse", torch.float32, 2, (B, Hq))
     st = _launch(q, (q, k_cache, v_cache, out, lse, workspace), _lib.load().fa_decode,
                  q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hkv,
                  Skv, d, _scale(scale, d), ns, workspace.data_ptr(), workspace.numel() * workspace.element_size())
@@ -179,8 +185,8 @@ def decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, 
         out = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    _need(out, "out", torch.bfloat16, 3)
-    _need(lse, "lse", torch.float32, 2)
+    _need(out, "out", torch.bfloat16, 3, (B, Hq, d))
+    _need(lse, "lse", torch.float32, 2, (B, Hq))
     st = _launch(q, (q, k_pages, v_pages, block_table, seq_lens, out, lse, workspace), _lib.load().fa_decode_paged,
                  q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), block_table.data_ptr(),
                  seq_lens.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, d, page_size, max_blocks,
@@ -253,11 +259,11 @@ def fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, vt8: torch.Tensor, q_scale: torc
             raise ValueError(f"{n} has shape {tuple(t.shape)}, expected {shp}")
     if out is None:
         out = torch.empty((B, Sq, Hq, d), dtype=torch.bfloat16, device=q8.device)
-    _need(out, "out", torch.bfloat16, 4)
+    _need(out, "out", torch.bfloat16, 4, (B, Sq, Hq, d))
     if return_lse and lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q8.device)
     if lse is not None:
-        _need(lse, "lse", torch.float32, 3)
+        _need(lse, "lse", torch.float32, 3, (B, Hq, Sq))
     st = _launch(q8, (q8, k8, vt8, q_scale, k_scale, v_scale, out, lse), _lib.load().fa_fwd_fp8,
                  q8.data_ptr(), k8.data_ptr(), vt8.data_ptr(), q_scale.data_ptr(), k_scale.data_ptr(),
                  v_scale.data_ptr(), out.data_ptr(), lse.data_ptr() if lse is not None else None, B, Hq, Hkv, Sq,
@@ -299,7 +305,7 @@ def bpt_layer(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w1: torch.Tenso
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if out is None:
         out = torch.empty((B, S, dm), dtype=torch.bfloat16, device=q.device)
-    _need(out, "out", torch.bfloat16, 3)
+    _need(out, "out", torch.bfloat16, 3, (B, S, dm))
     st = _launch(q, (q, k, v, w1, b1, w2, b2, out, workspace), _lib.load().fa_bpt_layer,
                  q.data_ptr(), k.data_ptr(), v.data_ptr(), w1.data_ptr(), b1.data_ptr(), w2.data_ptr(),
                  b2.data_ptr(), out.data_ptr(), B, Hq, Hkv, S, d, d_ff, int(bool(causal)), _scale(scale, d),
