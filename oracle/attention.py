@@ -78,9 +78,12 @@ def attention_rows(q_rows: np.ndarray, K: np.ndarray, V: np.ndarray, rows: np.nd
     rows = np.asarray(rows)
     Skv = K.shape[0]
     sigma = _sigma(scale)
-    s = sigma * (q_rows @ K.T)                                   # [n, Skv]
-    nvis = np.array([visible_keys(int(i), Sq, Skv, causal) for i in rows])
-    keep = np.arange(Skv)[None, :] < nvis[:, None]
+    nvis = np.array([visible_keys(int(i), Sq, Skv, causal) for i in rows], dtype=np.int64)
+    # keys past the largest visible count are masked for every row of the block (weight
+    # exactly 0), so only the first nk keys enter the products
+    nk = int(nvis.max()) if len(rows) else 0
+    s = sigma * (q_rows @ K[:nk].T)                              # [n, nk]
+    keep = np.arange(nk)[None, :] < nvis[:, None]
     s = np.where(keep, s, -np.inf)
     O = np.zeros((len(rows), V.shape[1]))
     LSE = np.full(len(rows), -np.inf)
@@ -90,7 +93,7 @@ def attention_rows(q_rows: np.ndarray, K: np.ndarray, V: np.ndarray, rows: np.nd
         M = sl.max(axis=1)
         w = np.exp(sl - M[:, None])                              # masked -> exp(-inf) = 0
         L = w.sum(axis=1)
-        O[live] = (w @ V) / L[:, None]
+        O[live] = (w @ V[:nk]) / L[:, None]
         LSE[live] = M + np.log(L)
     return O, LSE
 
@@ -130,43 +133,40 @@ def decode_ref(q: np.ndarray, kc: np.ndarray, vc: np.ndarray, *, scale: float):
     return O[:, 0], LSE[:, :, 0]
 
 
-def online_ref(q: np.ndarray, K: np.ndarray, V: np.ndarray, *, scale: float,
-               block: int = 2, per_element: bool = True):
-    """Streamed softmax for one query row, in the pages' running-statistics form.
+def online_ref(q: np.ndarray, K: np.ndarray, V: np.ndarray, *, scale: float, block: int = 2):
+    """Streamed softmax for one query row: the running-statistics form.
 
-    [ILP, Direct answer] and [IOP, FlashAttention]: walk the keys left to right
-    in blocks while keeping a running max m, a normaliser l and an output
-    accumulator acc. When a block raises the max, scale l and acc by
-    exp(m - m_new) before adding the block's terms; divide by l once at the end.
-    ``per_element`` updates the statistics after every key inside a block (as
-    the page's CPU example does); otherwise once per block.
+    [ILP, Direct answer] and [IOP, FlashAttention]: the keys are visited left to right
+    in blocks, and only three running quantities survive between blocks: the largest
+    scaled score m seen so far, the normaliser l = sum exp(s_j - m) and the accumulator
+    acc = sum exp(s_j - m) v_j over the keys seen. A block is first summarised by the
+    same three quantities over its own keys; the running state and the block summary
+    are then brought to their common maximum, each scaled by exp(its m - common m),
+    and added. The output is acc / l and the log-sum-exp m + ln l. ``block = 1``
+    updates the statistics after every key.
     Returns (o [d], lse) in float64.
     """
     sigma = _sigma(scale)
-    m, l = -math.inf, 0.0
-    acc = np.zeros(V.shape[1])
+    state = (-math.inf, 0.0, np.zeros(V.shape[1]))          # (m, l, acc) over no keys
     for j0 in range(0, K.shape[0], block):
-        Kb, Vb = K[j0:j0 + block], V[j0:j0 + block]
-        if per_element:
-            for kj, vj in zip(Kb, Vb):
-                s = sigma * float(np.dot(q, kj))
-                m_new = max(m, s)
-                c = math.exp(m - m_new) if m != -math.inf else 0.0
-                p = math.exp(s - m_new)
-                l = l * c + p
-                acc = acc * c + p * vj
-                m = m_new
-        else:
-            s = sigma * (Kb @ q)
-            m_new = max(m, float(s.max()))
-            c = math.exp(m - m_new) if m != -math.inf else 0.0
-            p = np.exp(s - m_new)
-            l = l * c + float(p.sum())
-            acc = acc * c + p @ Vb
-            m = m_new
+        scores = sigma * (K[j0:j0 + block] @ q)
+        m_blk = float(scores.max())
+        e_blk = np.exp(scores - m_blk)
+        summary = (m_blk, float(e_blk.sum()), e_blk @ V[j0:j0 + block])
+        state = _merge_running(state, summary)
+    m, l, acc = state
     if l == 0.0:
         return np.zeros(V.shape[1]), -math.inf
     return acc / l, m + math.log(l)
+
+
+def _merge_running(a, b):
+    """Two (m, l, acc) summaries of disjoint key sets -> the summary of their union.
+    A summary of no keys has m = -inf and weight 0 (never exponentiated)."""
+    m = max(a[0], b[0])
+    wa = math.exp(a[0] - m) if a[0] != -math.inf else 0.0
+    wb = math.exp(b[0] - m) if b[0] != -math.inf else 0.0
+    return m, wa * a[1] + wb * b[1], wa * a[2] + wb * b[2]
 
 
 def split_partials_ref(q: np.ndarray, kc: np.ndarray, vc: np.ndarray, *, scale: float,
