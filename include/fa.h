@@ -141,6 +141,30 @@ int fa_decode_partials(const void* q, const void* k_cache, const void* v_cache,
 int fa_decode_combine(const float* part_o, const float* part_lse, void* o, float* lse,
                       int B, int Hq, int d, int num_splits, void* stream);
 
+/* Bytes of device scratch behind fa_decode_noalloc (16 MiB per GPU). */
+#define FA_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * fa_decode_noalloc - fa_decode for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). Same arguments, results and errors as fa_decode without the
+ * workspace: the chunk partials go to a scratch array inside the library, one
+ * copy per GPU, FA_NOALLOC_SCRATCH_BYTES long, held until the process ends. Its
+ * address is looked up once per device on the first call made with that device
+ * current; later calls allocate nothing and call no allocating routine.
+ *  - The current device must be the device of `stream` and of every pointer.
+ *  - Calls whose fa_decode_workspace_bytes(B, Hq, d, num_splits) exceeds
+ *    FA_NOALLOC_SCRATCH_BYTES return FA_ERR_WORKSPACE and launch nothing.
+ *  - Every call on one GPU shares that GPU's scratch: calls that overlap on one
+ *    GPU (different streams, or threads without ordering) race and give
+ *    undefined results. Calls ordered on one stream are safe; each call writes
+ *    every partial it reads, so nothing needs clearing between calls.
+ * Returns FA_OK or a fa_status error code (FA_ERR_HIP if the scratch address
+ * cannot be obtained).
+ */
+int fa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                      int B, int Hq, int Hkv, int Skv, int d, float scale, int num_splits, void* stream);
+
 /*
  * fa_decode_paged - one decode step over a paged KV cache (the paged KV layout
  * that "I/O-Aware Kernels", section FlashAttention, mentions for FlashInfer's

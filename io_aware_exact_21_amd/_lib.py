@@ -24,6 +24,8 @@ SIGNATURES = {
     "fa_decode": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                           c_int, c_int, c_int, c_int, c_int, c_float,
                           c_int, c_void_p, c_size_t, c_void_p]),
+    "fa_decode_noalloc": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                  c_int, c_int, c_int, c_int, c_int, c_float, c_int, c_void_p]),
     "fa_decode_partials": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                    c_int, c_int, c_int, c_int, c_int, c_float, c_int, c_void_p]),
     "fa_decode_combine": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p,

@@ -120,6 +120,31 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, scale=
     return out, lse
 
 
+def decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, scale=None,
+                   num_splits: int = 0, out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """Split-KV decode whose partials live in the library's per-GPU scratch (fa_decode_noalloc):
+    the library allocates nothing. Pass ``out`` and ``lse`` to keep the call allocation-free
+    on this side too. Calls that overlap on one GPU race (see include/fa.h)."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    B, Hq, d = q.shape
+    Skv, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if tuple(k_cache.shape) != (B, Skv, Hkv, d) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache/v_cache shape does not match q")
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.bfloat16, 3, (B, Hq, d))
+    _need(lse, "lse", torch.float32, 2, (B, Hq))
+    st = _launch(q, (q, k_cache, v_cache, out, lse), _lib.load().fa_decode_noalloc,
+                 q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hkv,
+                 Skv, d, _scale(scale, d), int(num_splits))
+    _lib.check(st, "fa_decode_noalloc")
+    return out, lse
+
+
 def decode_partials(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, num_splits: int,
                     scale=None):
     """Chunk partials only: (part_o fp32 [B,Hq,n,d], part_lse fp32 [B,Hq,n])."""

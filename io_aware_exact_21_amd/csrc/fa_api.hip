@@ -4,11 +4,20 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "fa.h"
 #include "fa_bpt.hpp"
 #include "fa_bwd.hpp"
 #include "fa_fp8.hpp"
 #include "fa_launch.hpp"
+
+// Device memory the allocation-free decode (fa_decode_noalloc) uses for its chunk
+// partials. Each GPU the library runs on holds one copy until the process ends. In host
+// code the array's name is only a stand-in: its device address is obtained once per
+// device with hipGetSymbolAddress (with that device current) and kept in scratch_addr.
+static __device__ __align__(256) unsigned char scratch[FA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -138,6 +147,49 @@ int paged_partials_impl(const void* q, const void* k_pages, const void* v_pages,
   return FA_OK;
 }
 
+// Argument checks of one decode step (everything but the workspace).
+int decode_checks(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int Hq,
+                  int Hkv, int Skv, int d, int nsplit) {
+  int st = decode_args(q, k, v, B, Hq, Hkv, Skv, d, nsplit);
+  if (st != FA_OK) return st;
+  if (!o) return FA_ERR_NULL;
+  if (!aligned16(o) || (lse && !aligned16(lse))) return FA_ERR_ALIGN;
+  return FA_OK;
+}
+
+// Chunk partials into `workspace` (laid out as fa_decode_workspace_bytes describes), then the merge.
+int decode_launch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Skv,
+                  int d, float scale, int nsplit, void* workspace, hipStream_t s) {
+  float* part_o = static_cast<float*>(workspace);
+  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                             align256((size_t)B * Hq * nsplit * d * sizeof(float)));
+  int st = partials_impl(q, k, v, part_o, part_lse, B, Hq, Hkv, Skv, d, scale, nsplit, s);
+  if (st != FA_OK) return st;
+  return combine_impl(part_o, part_lse, o, lse, B, Hq, d, nsplit, s);
+}
+
+// ---- scratch of the allocation-free decode ------------------------------------------
+constexpr int kMaxDevices = 64;
+std::atomic<void*> scratch_addr[kMaxDevices];
+std::mutex scratch_mu;
+
+// Device address of the current device's scratch array (looked up on the first call per device).
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_HIP;
+  void* ptr = scratch_addr[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    ptr = scratch_addr[dev].load(std::memory_order_relaxed);
+    if (ptr == nullptr) {
+      if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return FA_ERR_HIP;
+      scratch_addr[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return FA_OK;
+}
+
 int log2_exact(int x) {
   int l = 0;
   while ((1 << l) < x && l < 30) ++l;
@@ -217,20 +269,27 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, 
               int Hkv, int Skv, int d, float scale, int num_splits, void* workspace, size_t workspace_bytes,
               void* stream) {
   if (num_splits <= 0) num_splits = fa_decode_default_splits(B, Hkv, Skv, d);
-  int st = decode_args(q, k_cache, v_cache, B, Hq, Hkv, Skv, d, num_splits);
+  int st = decode_checks(q, k_cache, v_cache, o, lse, B, Hq, Hkv, Skv, d, num_splits);
   if (st != FA_OK) return st;
-  if (!o) return FA_ERR_NULL;
-  if (!aligned16(o) || (lse && !aligned16(lse))) return FA_ERR_ALIGN;
   const size_t need = fa_decode_workspace_bytes(B, Hq, d, num_splits);
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || workspace_bytes < need)
     return FA_ERR_WORKSPACE;
-  float* part_o = static_cast<float*>(workspace);
-  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                             align256((size_t)B * Hq * num_splits * d * sizeof(float)));
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  st = partials_impl(q, k_cache, v_cache, part_o, part_lse, B, Hq, Hkv, Skv, d, scale, num_splits, s);
+  return decode_launch(q, k_cache, v_cache, o, lse, B, Hq, Hkv, Skv, d, scale, num_splits, workspace,
+                       static_cast<hipStream_t>(stream));
+}
+
+int fa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse, int B, int Hq,
+                      int Hkv, int Skv, int d, float scale, int num_splits, void* stream) {
+  if (num_splits <= 0) num_splits = fa_decode_default_splits(B, Hkv, Skv, d);
+  int st = decode_checks(q, k_cache, v_cache, o, lse, B, Hq, Hkv, Skv, d, num_splits);
   if (st != FA_OK) return st;
-  return combine_impl(part_o, part_lse, o, lse, B, Hq, d, num_splits, s);
+  // the limit is checked before the device is touched, so an oversized call launches nothing
+  if (fa_decode_workspace_bytes(B, Hq, d, num_splits) > (size_t)FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != FA_OK) return st;
+  return decode_launch(q, k_cache, v_cache, o, lse, B, Hq, Hkv, Skv, d, scale, num_splits, ws,
+                       static_cast<hipStream_t>(stream));
 }
 
 int fa_decode_paged(const void* q, const void* k_pages, const void* v_pages, const int* block_table,

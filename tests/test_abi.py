@@ -232,3 +232,19 @@ def test_bpt_validation(lib):
     assert f(rows=128) == FA_ERR_WORKSPACE       # workspace sized for 64-row blocks
     assert f(ws=A + 16) == FA_ERR_ALIGN
     assert f(q=A + 8) == FA_ERR_ALIGN
+
+
+def test_decode_noalloc_validation(lib):
+    """The allocation-free decode validates like fa_decode and refuses, before touching any
+    device, a shape whose partials exceed its fixed scratch."""
+    from io_aware_exact_21_amd._lib import FA_ERR_ALIGN, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_WORKSPACE
+
+    def dec(q=A, o=A, B=2, Hq=8, Hkv=2, Skv=100, d=128, ns=4):
+        return lib.fa_decode_noalloc(q, A, A, o, None, B, Hq, Hkv, Skv, d, 0.1, ns, None)
+    assert dec(q=None) == FA_ERR_NULL
+    assert dec(o=None) == FA_ERR_NULL
+    assert dec(Hq=7) == FA_ERR_SHAPE
+    assert dec(o=A + 4) == FA_ERR_ALIGN
+    limit = 16 << 20
+    assert lib.fa_decode_workspace_bytes(64, 32, 128, 40) > limit
+    assert dec(B=64, Hq=32, Hkv=8, Skv=64 * 40, ns=40) == FA_ERR_WORKSPACE
