@@ -26,6 +26,7 @@
 // (ds_read_b64_tr_b16) use one XOR swizzle that is free of bank conflicts in both modes.
 #include "fa_bwd.hpp"
 #include "fa_device.hpp"
+#include "fa_dma.hpp"
 
 namespace fa {
 
@@ -36,40 +37,12 @@ constexpr int kBwdStages = 3;    // LDS ring depth (tiles, dQ kernel)
 constexpr int kBwdDkvTile = 128; // Q / dO rows per dK/dV tile (two-stage ring)
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) unsigned char lds_u8;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
-
-__device__ __forceinline__ unsigned lds_addr(const void* p) {
-  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-__device__ __forceinline__ const lds_u8* lds_ptr(unsigned a) { return (const lds_u8*)(uintptr_t)a; }
-
-// Wave-level direct global -> LDS copies (lane i's bytes at base + voff_i land at LDS
-// byte lds + i * size). Issued as inline assembly so the compiler does not order LDS
-// reads of other ring stages behind them; completion is tracked with wait_vmcnt plus a
-// barrier. m0 is written only here.
-__device__ __forceinline__ void dma16(const void* base, unsigned voff, unsigned lds) {
-  const unsigned m = __builtin_amdgcn_readfirstlane(lds);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(base), "s"(m)
-               : "memory");
-}
-__device__ __forceinline__ void dma4(const void* base, unsigned voff, unsigned lds) {
-  const unsigned m = __builtin_amdgcn_readfirstlane(lds);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
-               :
-               : "v"(voff), "s"(base), "s"(m)
-               : "memory");
-}
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
+using dma::lds_addr;
+using dma::lds_ptr;
+using dma::lds_u8;
+using dma::wait_vmcnt;
 
 // 16-byte chunk c of tile row r is stored at chunk c ^ bswz(r). Row reads: 16 lanes
 // read 16 consecutive rows at one chunk, so bswz must permute 16 consecutive rows
@@ -203,13 +176,13 @@ struct TileDma {
     const uint16_t* t = base + (int64_t)r0 * row_stride;
     if (r0 + BT <= rmax) {
 #pragma unroll
-      for (int n = 0; n < NPW; ++n) dma16(t, off[n], dst + (w + NW * n) * 1024);
+      for (int n = 0; n < NPW; ++n) dma::copy16(t, off[n], dst + (w + NW * n) * 1024);
     } else {
 #pragma unroll
       for (int n = 0; n < NPW; ++n) {
         const int r = row_of(n, w, lane);
         const unsigned ro = (unsigned)((int64_t)min(r, rmax - 1 - r0) * row_stride * 2);
-        dma16(t, ro + (((lane % CPR) ^ bswz<D>(r)) << 4), dst + (w + NW * n) * 1024);
+        dma::copy16(t, ro + (((lane % CPR) ^ bswz<D>(r)) << 4), dst + (w + NW * n) * 1024);
       }
     }
   }
@@ -429,8 +402,8 @@ __global__ __launch_bounds__(kBwdDkvWaves * 64) void fa_bwd_dkdv_kernel(BwdParam
     const int64_t soff = ((int64_t)b * p.Hq + hq) * p.Sq + r0;
     const int half = w >> 1;
     const unsigned ro = (unsigned)min(64 * half + lane, p.Sq - 1 - r0) * 4u;
-    if ((w & 1) == 0) dma4(p.lse + soff, ro, lse_ring + st * VB + 256u * half);
-    else dma4(p.dsum + soff, ro, dsum_ring + st * VB + 256u * half);
+    if ((w & 1) == 0) dma::copy4(p.lse + soff, ro, lse_ring + st * VB + 256u * half);
+    else dma::copy4(p.dsum + soff, ro, dsum_ring + st * VB + 256u * half);
   };
 
   f32x16 dk[D / 32], dv[D / 32];

@@ -16,6 +16,7 @@
 // softmax of unit u + 1, so MFMA and VALU work of one wave overlap; the second wave
 // on each SIMD fills the remaining gaps.
 #include "fa_device.hpp"
+#include "fa_dma.hpp"
 #include "fa_launch.hpp"
 
 namespace fa {
@@ -30,34 +31,11 @@ constexpr int kFwdStages = 3;     // LDS ring depth (tiles)
 // running max only has to move when a row's scores jump by more than 64 (log2 units).
 constexpr float kRescaleBound = 18446744073709551616.0f;   // 2^64
 
-typedef __attribute__((address_space(3))) unsigned char lds_u8;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-
-__device__ __forceinline__ unsigned lds_addr(const void* p) {
-  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-__device__ __forceinline__ const lds_u8* lds_ptr(unsigned a) { return (const lds_u8*)(uintptr_t)a; }
-
-// One wave-level direct global -> LDS copy: lane i fetches the 16 bytes at
-// base + voff_i and the wave writes them to 64 consecutive 16-byte LDS chunks starting
-// at byte address `lds` (wave-uniform, passed in m0). Issued as inline assembly so
-// that the compiler does not serialise later LDS reads of other ring stages behind
-// it; completion is tracked explicitly with wait_vmcnt + a barrier. m0 is written
-// only here: no other code in these kernels uses it.
-__device__ __forceinline__ void lds_dma16(const void* base, unsigned voff, unsigned lds) {
-  const unsigned m = __builtin_amdgcn_readfirstlane(lds);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(base), "s"(m)
-               : "memory");
-}
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
+using dma::lds_addr;
+using dma::lds_ptr;
+using dma::lds_u8;
+using dma::wait_vmcnt;
 
 // LDS ring: the NS K tiles first, then the NS V tiles (BCT keys x D bf16 each, row-major,
 // 16-byte chunks XOR-swizzled by key). Keeping K and V apart keeps every operand read
@@ -107,8 +85,8 @@ struct KvDma {
     if (k0 + BCT <= kmax) {
 #pragma unroll
       for (int n = 0; n < NPW; ++n) {
-        lds_dma16(kt, koff[n], kst + (w + NW * n) * 1024);
-        lds_dma16(vt, voff[n], vst + (w + NW * n) * 1024);
+        dma::copy16(kt, koff[n], kst + (w + NW * n) * 1024);
+        dma::copy16(vt, voff[n], vst + (w + NW * n) * 1024);
       }
     } else {
       const int cl = lane % CPR;
@@ -116,8 +94,8 @@ struct KvDma {
       for (int n = 0; n < NPW; ++n) {
         const int key = key_of(n, w, lane);
         const unsigned roff = (unsigned)((int64_t)min(key, kmax - 1 - k0) * row_stride * 2);
-        lds_dma16(kt, roff + ((cl ^ k_swz<D>(key)) << 4), kst + (w + NW * n) * 1024);
-        lds_dma16(vt, roff + ((cl ^ v_swz<D>(key)) << 4), vst + (w + NW * n) * 1024);
+        dma::copy16(kt, roff + ((cl ^ k_swz<D>(key)) << 4), kst + (w + NW * n) * 1024);
+        dma::copy16(vt, roff + ((cl ^ v_swz<D>(key)) << 4), vst + (w + NW * n) * 1024);
       }
     }
   }
