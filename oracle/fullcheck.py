@@ -1,0 +1,282 @@
+"""Whole-tensor comparison of device results with the fp64 oracle, over a process pool.
+
+TEST INFRASTRUCTURE ONLY, like the rest of this package: the tests and the benchmark's
+oracle leg use it; the library never does.
+
+The stated check for bf16 I/O with fp32 accumulation is max-abs <= 1e-2 and relative
+L2 <= 4e-3 for O and for the finite LSE entries, over the whole tensor, with -inf LSE
+entries matching exactly. A bf16 output cannot come closer to the exact value than
+half a bf16 spacing, which exceeds 1e-2 once |O| >= 4, so next to the stated check
+this module reports:
+  * the floor: max |RNE_bf16(O_ref) - O_ref|, what a correctly rounded O would miss by;
+  * the worst element's error in bf16 ulps (spacings at its exact value);
+  * the same check on an fp32 output of the same kernel (no output rounding).
+A config gets the label "pass" when the stated check holds as written. A miss of the
+O max-abs is labelled "floor-limited" only when every element beyond 1e-2 lies within
+one bf16 ulp of O_ref, the rel-L2 and LSE checks hold, and the fp32-output run passes
+the stated check as written; anything else is "fail".
+
+Work is split by (batch, query head) -- or, for decode, by batch element -- and each
+worker runs the oracle on its share and returns only error statistics, which add up
+over shares. Workers are separate spawned interpreters with one BLAS thread each; start
+the pool before the calling process initialises a GPU.
+"""
+from __future__ import annotations
+
+import math
+import multiprocessing as mp
+import os
+import time
+
+import numpy as np
+
+from .attention import attention_rows, kv_head_of, visible_keys, widen_bf16
+
+MAX_ABS = 1e-2
+REL_L2 = 4e-3
+ROW_BLOCK = 512
+
+_pool = None
+_pool_size = 0
+
+
+# ---------------------------------------------------------------- pool
+def _init_worker() -> None:
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(limits=1)
+    except Exception:
+        pass
+
+
+def pool_workers() -> int:
+    """Workers for this host: its CPU affinity, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def start_pool(n: int | None = None):
+    """Start (once) the spawned worker pool and return it."""
+    global _pool, _pool_size
+    if _pool is None:
+        _pool_size = n or pool_workers()
+        _pool = mp.get_context("spawn").Pool(_pool_size, initializer=_init_worker)
+    return _pool
+
+
+def pool_size() -> int:
+    return _pool_size
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# ---------------------------------------------------------------- statistics
+def bf16_ulp(x: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 values (8 significant bits) at |x|; normal range assumed below 2^-126."""
+    e = np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -126)))
+    return np.ldexp(1.0, (e - 7).astype(np.int64))
+
+
+def bf16_rne(x: np.ndarray) -> np.ndarray:
+    """float64 -> nearest bf16 value (ties to even), as float64."""
+    sp = bf16_ulp(x)
+    return np.rint(x / sp) * sp
+
+
+def o_stats(o: np.ndarray, ref: np.ndarray) -> dict:
+    """Mergeable error statistics of one output share against the oracle."""
+    o = np.asarray(o, dtype=np.float64)
+    err = np.abs(o - ref)
+    fin = np.isfinite(o)
+    ulp = bf16_ulp(ref)
+    over = err > MAX_ABS
+    err_f = np.where(fin, err, np.inf)                       # a non-finite output counts as infinitely wrong
+    worst = int(np.argmax(err_f)) if err.size else 0
+    return {"n": int(err.size), "nonfinite": int((~fin).sum()),
+            "sse": float(np.square(np.where(fin, o - ref, 0.0)).sum()), "ssr": float(np.square(ref).sum()),
+            "max_abs": float(err_f.flat[worst]) if err.size else 0.0,
+            "ulps_at_max": float(err_f.flat[worst] / ulp.flat[worst]) if err.size else 0.0,
+            "ref_at_max": float(ref.flat[worst]) if err.size else 0.0,
+            "floor": float(np.abs(bf16_rne(ref) - ref).max()) if err.size else 0.0,
+            "over": int(over.sum()), "over_beyond_ulp": int((over & (err > ulp)).sum()),
+            "widened_bad": int((err > MAX_ABS + 0.5 * ulp).sum())}
+
+
+def lse_stats(lse: np.ndarray, ref: np.ndarray) -> dict:
+    lse = np.asarray(lse, dtype=np.float64)
+    ninf = np.isneginf(ref)
+    g, r = lse[~ninf], ref[~ninf]
+    err = np.abs(g - r)
+    return {"n": int(g.size), "ninf_mismatch": int((np.isneginf(lse) != ninf).sum()),
+            "nonfinite": int((~np.isfinite(g)).sum()),
+            "sse": float(np.square(np.where(np.isfinite(g), g - r, 0.0)).sum()), "ssr": float(np.square(r).sum()),
+            "max_abs": float(np.where(np.isfinite(err), err, np.inf).max()) if g.size else 0.0}
+
+
+def merge_stats(parts: list) -> dict:
+    if not parts:
+        return {}
+    out = {}
+    top = max(parts, key=lambda p: p["max_abs"])           # the share holding the worst element
+    for k in parts[0]:
+        if k in ("max_abs", "ulps_at_max", "ref_at_max"):
+            out[k] = top[k]
+        elif k == "floor":
+            out[k] = max(p[k] for p in parts)
+        else:
+            out[k] = sum(p[k] for p in parts)
+    return out
+
+
+def summarise(o: dict, lse: dict | None) -> dict:
+    """Stated-check numbers of merged statistics."""
+    rel_o = math.sqrt(o["sse"] / o["ssr"]) if o["ssr"] > 0 else math.sqrt(o["sse"])
+    res = {"O_max_abs": o["max_abs"], "O_rel_l2": rel_o, "O_floor": o["floor"],
+           "O_worst_error_bf16_ulps": o["ulps_at_max"], "O_ref_at_worst": o["ref_at_max"],
+           "O_over_1e-2": o["over"], "O_over_1e-2_beyond_1ulp": o["over_beyond_ulp"],
+           "O_widened_bound_misses": o["widened_bad"], "O_nonfinite": o["nonfinite"], "O_elements": o["n"]}
+    if lse is not None:
+        rel_l = math.sqrt(lse["sse"] / lse["ssr"]) if lse["ssr"] > 0 else math.sqrt(lse["sse"])
+        res.update({"LSE_max_abs": lse["max_abs"], "LSE_rel_l2": rel_l, "LSE_ninf_mismatch": lse["ninf_mismatch"],
+                    "LSE_nonfinite": lse["nonfinite"], "LSE_finite_entries": lse["n"]})
+    return res
+
+
+def stated_ok(s: dict) -> bool:
+    ok = s["O_nonfinite"] == 0 and s["O_max_abs"] <= MAX_ABS and s["O_rel_l2"] <= REL_L2
+    if "LSE_max_abs" in s:
+        ok = ok and s["LSE_ninf_mismatch"] == 0 and s["LSE_nonfinite"] == 0 and s["LSE_max_abs"] <= MAX_ABS \
+            and s["LSE_rel_l2"] <= REL_L2
+    return ok
+
+
+def label(bf16: dict, f32: dict | None) -> str:
+    """'pass', 'floor-limited' or 'fail' for a bf16-output summary (see the module docstring)."""
+    if stated_ok(bf16):
+        return "pass"
+    rest = dict(bf16, O_max_abs=0.0)                 # everything but the O max-abs
+    if stated_ok(rest) and bf16["O_over_1e-2_beyond_1ulp"] == 0 and f32 is not None and stated_ok(f32):
+        return "floor-limited"
+    return "fail"
+
+
+# ---------------------------------------------------------------- worker
+def _oracle_rows(q_bits, k_bits, v_bits, rows, Sq, causal, scale):
+    Q, K, V = widen_bf16(q_bits), widen_bf16(k_bits), widen_bf16(v_bits)
+    O = np.zeros((len(rows), Q.shape[1]))
+    L = np.full(len(rows), -np.inf)
+    for r0 in range(0, len(rows), ROW_BLOCK):
+        sl = slice(r0, r0 + ROW_BLOCK)
+        O[sl], L[sl] = attention_rows(Q[sl], K, V, rows[sl], Sq, causal, scale)
+    return O, L
+
+
+def _share_task(args):
+    """One share: oracle O, LSE for its query rows, then error statistics of each device output."""
+    key, q_bits, k_bits, v_bits, rows, Sq, causal, scale, outputs = args
+    t0 = time.perf_counter()
+    O, L = _oracle_rows(q_bits, k_bits, v_bits, rows, Sq, causal, scale)
+    dt = time.perf_counter() - t0
+    stats = {}
+    for name, o, lse in outputs:
+        stats[name] = (o_stats(o, O), lse_stats(lse, L) if lse is not None else None)
+    return key, stats, dt
+
+
+def _decode_task(args):
+    """One batch element of a decode step: every query head against its KV head."""
+    key, q_bits, k_bits, v_bits, Hkv, scale, outputs = args
+    Hq = q_bits.shape[0]
+    t0 = time.perf_counter()
+    O = np.zeros((Hq, q_bits.shape[1]))
+    L = np.full(Hq, -np.inf)
+    for h in range(Hq):
+        hk = kv_head_of(h, Hq, Hkv)
+        o, l = attention_rows(widen_bf16(q_bits[h:h + 1]), widen_bf16(k_bits[:, hk]), widen_bf16(v_bits[:, hk]),
+                              np.zeros(1, dtype=np.int64), 1, False, scale)
+        O[h], L[h] = o[0], l[0]
+    dt = time.perf_counter() - t0
+    stats = {name: (o_stats(o, O), lse_stats(lse, L)) for name, o, lse in outputs}
+    return key, stats, dt
+
+
+# ---------------------------------------------------------------- drivers
+def prefill_flops(Sq: int, Skv: int, d: int, causal: bool) -> float:
+    """Counted FLOPs of one (batch, head) under the 4 d per visible (query, key) rule."""
+    if causal:
+        nvis = sum(visible_keys(i, Sq, Skv, True) for i in range(Sq))
+    else:
+        nvis = Sq * Skv
+    return 4.0 * d * nvis
+
+
+def check_prefill(q, k, v, outputs: dict, *, causal: bool, scale: float, heads=None, progress=None) -> dict:
+    """Compare device outputs of a prefill with the oracle over every (batch, head) (or ``heads``).
+
+    q [B,Sq,Hq,d], k and v [B,Skv,Hkv,d] are bf16 bit arrays (uint16); ``outputs`` maps a
+    name to (O [B,Sq,Hq,d] float32 or float64, LSE [B,Hq,Sq] or None). Returns, per
+    output name, the merged statistics summary, plus timing of the oracle itself.
+    """
+    B, Sq, Hq, d = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    heads = [(b, h) for b in range(B) for h in range(Hq)] if heads is None else list(heads)
+    rows = np.arange(Sq)
+
+    def tasks():
+        for b, h in heads:
+            hk = kv_head_of(h, Hq, Hkv)
+            outs = [(name, np.ascontiguousarray(o[b, :, h, :]),
+                     None if lse is None else np.ascontiguousarray(lse[b, h, :])) for name, (o, lse) in outputs.items()]
+            yield ((b, h), np.ascontiguousarray(q[b, :, h, :]), np.ascontiguousarray(k[b, :, hk, :]),
+                   np.ascontiguousarray(v[b, :, hk, :]), rows, Sq, causal, scale, outs)
+
+    return _run(_share_task, tasks(), len(heads), list(outputs), prefill_flops(Sq, Skv, d, causal), progress)
+
+
+def check_decode(q, k, v, outputs: dict, *, scale: float, batches=None, progress=None) -> dict:
+    """Decode: q [B,Hq,d], caches [B,Skv,Hkv,d] (bf16 bits); outputs name -> (O [B,Hq,d], LSE [B,Hq])."""
+    B, Hq, d = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    batches = range(B) if batches is None else list(batches)
+
+    def tasks():
+        for b in batches:
+            outs = [(name, np.ascontiguousarray(o[b]), np.ascontiguousarray(lse[b])) for name, (o, lse) in outputs.items()]
+            yield (b, np.ascontiguousarray(q[b]), np.ascontiguousarray(k[b]), np.ascontiguousarray(v[b]), Hkv, scale, outs)
+
+    return _run(_decode_task, tasks(), len(batches), list(outputs), 4.0 * d * Skv * Hq, progress)
+
+
+def _run(fn, tasks, ntasks: int, names: list, flops_per_task: float, progress) -> dict:
+    pool = start_pool()
+    parts = {n: ([], []) for n in names}
+    busy = 0.0
+    t0 = time.perf_counter()
+    done = 0
+    for _, stats, dt in pool.imap_unordered(fn, tasks, chunksize=1):
+        busy += dt
+        for n, (so, sl) in stats.items():
+            parts[n][0].append(so)
+            if sl is not None:
+                parts[n][1].append(sl)
+        done += 1
+        if progress is not None and (done == ntasks or done % max(1, ntasks // 8) == 0):
+            progress(f"oracle: {done}/{ntasks} shares, {time.perf_counter() - t0:.1f} s")
+    wall = time.perf_counter() - t0
+    res = {n: summarise(merge_stats(po), merge_stats(pl) if pl else None) for n, (po, pl) in parts.items()}
+    res["_oracle"] = {"shares": ntasks, "wall_s": wall, "worker_busy_s": busy, "workers": pool_size(),
+                      "flops": flops_per_task * ntasks, "gflops_per_s": flops_per_task * ntasks / wall / 1e9,
+                      "cpu_model": cpu_model()}
+    return res

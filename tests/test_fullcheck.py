@@ -1,0 +1,88 @@
+"""The whole-tensor stated check (oracle/fullcheck.py) on the CPU: its statistics, its
+pass / floor-limited / fail labels, and its process-pool drivers on small cases with
+outputs derived from the oracle itself (the correctly rounded answer must pass; a
+planted error must fail)."""
+import numpy as np
+import pytest
+
+from oracle import fullcheck as fc
+from oracle.attention import attention_ref, decode_ref, widen_bf16
+from synth import bf16_rne_bits, make_qkv
+
+
+def test_bf16_rounding_matches_the_input_recipe():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal(20000) * np.exp2(rng.integers(-20, 20, 20000))
+    np.testing.assert_array_equal(fc.bf16_rne(x), widen_bf16(bf16_rne_bits(x)))
+    assert fc.bf16_ulp(np.array([1.0, 1.5, 4.0, 5.9, -0.3]))[2] == 2.0 ** -5
+    assert fc.bf16_ulp(np.array([1.0]))[0] == 2.0 ** -7
+
+
+def _summ(o, ref, lse=None, lref=None):
+    return fc.summarise(fc.o_stats(o, ref), None if lse is None else fc.lse_stats(lse, lref))
+
+
+def test_labels():
+    ref = np.array([[5.3, 0.1, -0.7], [0.2, 0.3, 0.4]])
+    L = np.array([1.0, -np.inf])
+    good = _summ(ref + 1e-3, ref, L, L)
+    assert fc.label(good, None) == "pass"
+    rounded = _summ(fc.bf16_rne(ref), ref, L, L)       # 5.3 -> 5.3125: 0.0125 > 1e-2, within one ulp
+    assert rounded["O_max_abs"] > 1e-2 and rounded["O_over_1e-2_beyond_1ulp"] == 0
+    assert rounded["O_ref_at_worst"] == 5.3 and rounded["O_worst_error_bf16_ulps"] == pytest.approx(0.4)
+    assert rounded["O_widened_bound_misses"] == 0
+    assert fc.label(rounded, good) == "floor-limited"
+    assert fc.label(rounded, None) == "fail"           # no fp32 run: not labelled floor-limited
+    bad_f32 = _summ(ref + 2e-2, ref, L, L)
+    assert fc.label(rounded, bad_f32) == "fail"
+    two_ulps = ref.copy(); two_ulps[0, 0] += 2 * 2.0 ** -5
+    assert fc.label(_summ(two_ulps, ref, L, L), good) == "fail"
+    lse_bad = _summ(ref, ref, L + np.array([0.02, 0.0]), L)
+    assert fc.label(lse_bad, good) == "fail"
+    ninf_bad = _summ(ref, ref, np.array([1.0, 3.0]), L)
+    assert ninf_bad["LSE_ninf_mismatch"] == 1 and fc.label(ninf_bad, good) == "fail"
+    nan_o = ref.copy(); nan_o[1, 1] = np.nan
+    assert fc.label(_summ(nan_o, ref, L, L), good) == "fail"
+
+
+def test_merge_equals_whole():
+    rng = np.random.default_rng(2)
+    ref = rng.standard_normal((40, 8)); o = ref + rng.standard_normal((40, 8)) * 1e-3
+    whole = fc.summarise(fc.o_stats(o, ref), None)
+    parts = fc.summarise(fc.merge_stats([fc.o_stats(o[:13], ref[:13]), fc.o_stats(o[13:], ref[13:])]), None)
+    for k in whole:
+        assert whole[k] == pytest.approx(parts[k], rel=1e-12), k
+
+
+@pytest.fixture(scope="module")
+def pool():
+    return fc.start_pool(2 if fc._pool is None else None)
+
+
+def test_check_prefill_pool(pool):
+    """Pool driver on a causal GQA case: the oracle's own answer rounded to bf16 passes,
+    the same with one element moved by 0.05 fails."""
+    B, Hq, Hkv, S, d = 2, 4, 2, 70, 64
+    q, k, v = make_qkv(B, Hq, Hkv, S, S, d, seed=41)
+    O, L = attention_ref(widen_bf16(q), widen_bf16(k), widen_bf16(v), causal=True, scale=0.125)
+    o_bf = fc.bf16_rne(O).astype(np.float32)
+    res = fc.check_prefill(q, k, v, {"bf16": (o_bf, L.astype(np.float32)), "f32": (O.astype(np.float32), L)},
+                           causal=True, scale=0.125)
+    assert fc.label(res["bf16"], res["f32"]) == "pass"
+    assert res["bf16"]["O_elements"] == O.size and res["bf16"]["LSE_finite_entries"] == L.size
+    assert res["_oracle"]["shares"] == B * Hq
+    o_bad = o_bf.copy(); o_bad[1, 33, 3, 7] += 0.05
+    res = fc.check_prefill(q, k, v, {"bf16": (o_bad, L)}, causal=True, scale=0.125, heads=[(1, 3), (0, 0)])
+    assert res["bf16"]["O_max_abs"] > 0.04 and fc.label(res["bf16"], None) == "fail"
+
+
+def test_check_decode_pool(pool):
+    B, Hq, Hkv, Skv, d = 3, 8, 2, 300, 128
+    q, k, v = make_qkv(B, Hq, Hkv, 1, Skv, d, seed=42)
+    q = q.reshape(B, Hq, d)
+    O, L = decode_ref(widen_bf16(q), widen_bf16(k), widen_bf16(v), scale=d ** -0.5)
+    res = fc.check_decode(q, k, v, {"bf16": (fc.bf16_rne(O), L)}, scale=d ** -0.5)
+    assert fc.label(res["bf16"], None) == "pass" and res["bf16"]["O_elements"] == O.size
+    o_bad = fc.bf16_rne(O); o_bad[2, 5, 100] -= 0.03
+    res = fc.check_decode(q, k, v, {"bf16": (o_bad, L)}, scale=d ** -0.5)
+    assert fc.label(res["bf16"], None) == "fail"
