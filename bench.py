@@ -4,12 +4,21 @@ One step = one pass of the whole hot path on resident synthetic inputs:
   fa_fwd on the long-prefill workload (B2 H32 S8192 d128, causal, K x4 on 1% of positions),
   then the split-KV decode (B64 Hq32 Hkv8 Skv16384 d128): chunk partials + log-sum-exp merge.
 W untimed warmup steps (default 50), then K timed steps (default 100) between device
-synchronisations. Every kernel
-is bracketed by HIP events recorded on the stream the library launches on (torch's
-current stream, which is passed to the library), giving per-kernel average durations.
+synchronisations. Every kernel is bracketed by HIP events recorded on the stream the
+library launches on (torch's current stream, which is passed to the library), giving
+per-kernel average durations.
 
 Prints ONE JSON line. ``value`` is forward TFLOP/s with causal FLOPs counted as half
-(4*B*Hq*Sq*Skv*d/2); the decode figures sit under ``decode``.
+(4*B*Hq*Sq*Skv*d/2); the decode figures sit under ``decode``, the other prefill
+workloads (B4 H16 S2048 d64; B1 Hq32 Hkv8 S32768 d128) under ``prefill_other``, each
+timed on its own after the step loop. Beside the GPU figures:
+  * ``ceilings``: the sustained matrix-core rate and HBM read bandwidth measured on this
+    chip by the probe library, and each roofline's fraction of them;
+  * ``cpu_baseline`` per workload: the fp64 oracle as it stands, spread over a process pool
+    of the host's cores (one BLAS thread each), timed on a stated share of the workload;
+  * ``parity`` per workload: the stated check (max-abs <= 1e-2, rel-L2 <= 4e-3 for O and
+    LSE) over the same share, with the bf16 floor, the worst error in bf16 ulps and the
+    same check on an fp32-output run of the forward.
 """
 from __future__ import annotations
 
@@ -89,33 +98,136 @@ def measured_mfma_util(name: str, family: str):
             "source": "rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs), sustained dispatches"}
 
 
-def cpu_baseline(w, q, k, v, budget_s: float) -> dict:
-    """The fp64 oracle, as it stands, on whole heads of the same workload until the budget is used."""
-    import numpy as np
-    from oracle.attention import attention_rows, kv_head_of, widen_bf16
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
-    except Exception:
-        threads = 1
-    flops, heads, t0 = 0.0, 0, time.perf_counter()
-    order = [(b, h) for h in range(w.Hq) for b in range(w.B)]
-    for b, h in order:
-        hk = kv_head_of(h, w.Hq, w.Hkv)
-        K, V = widen_bf16(k[b, :, hk, :]), widen_bf16(v[b, :, hk, :])
-        for r0 in range(0, w.Sq, 512):
-            rows = np.arange(r0, min(w.Sq, r0 + 512))
-            attention_rows(widen_bf16(q[b, rows, h, :]), K, V, rows, w.Sq, w.causal, w.scale)
-        nvis = (np.minimum(np.arange(w.Sq) + w.Skv - w.Sq + 1, w.Skv).clip(0).sum() if w.causal
-                else w.Sq * w.Skv)
-        flops += 4.0 * w.d * float(nvis)
-        heads += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{heads} whole (batch, head) slices of the {w.name} workload "
-                      f"({heads * w.Sq} query rows, all visible keys), fp64 NumPy oracle, {dt:.1f} s"}
+# Share of each workload the oracle leg covers: every (batch, head) except on the 32k GQA
+# prefill, where half of the query heads (every second one, all KV heads) keep the leg
+# within about a minute on 16 host cores. The whole-tensor tests cover every head.
+ORACLE_SHARE = {"gqa32k": lambda w: [(0, h) for h in range(0, w.Hq, 2)]}
+
+
+def oracle_leg(key: str, w, q, k, v, outputs: dict) -> tuple:
+    """The fp64 oracle as it stands, over a process pool of the host's cores, on the
+    workload's share (ORACLE_SHARE): its rate (cpu_baseline) and the stated check of the
+    device outputs on that share (parity)."""
+    from oracle import fullcheck as fc
+    log = lambda m: print(f"[bench] {key}: {m}", file=sys.stderr, flush=True)
+    if w.decode:
+        res = fc.check_decode(q, k, v, outputs, scale=w.scale, progress=log)
+        share, total = w.B, w.B
+        what = f"{share} of {total} sequences (every query head)"
+        unit_amount = decode_bytes(w)["total"] * share / total
+        value, unit = unit_amount / res["_oracle"]["wall_s"] / 1e9, "GB/s"
+    else:
+        heads = ORACLE_SHARE[key](w) if key in ORACLE_SHARE else None
+        res = fc.check_prefill(q, k, v, outputs, causal=w.causal, scale=w.scale, heads=heads, progress=log)
+        share, total = res["_oracle"]["shares"], w.B * w.Hq
+        what = f"{share} of {total} (batch, query head) slices, every query row and visible key"
+        value, unit = res["_oracle"]["flops"] / res["_oracle"]["wall_s"] / 1e12, "TFLOP/s"
+    orc = res.pop("_oracle")
+    cpu = {"value": round(value, 5), "unit": unit, "cores": orc["workers"], "kind": "oracle",
+           "cpu_model": orc["cpu_model"], "wall_s": round(orc["wall_s"], 2),
+           "sample": f"{what} of the {w.name} workload; fp64 NumPy oracle in {orc['workers']} worker "
+                     f"processes with one BLAS thread each"}
+    par = {"share": what, "label": fc.label(res["bf16"], res.get("f32")), "bf16_output": res["bf16"]}
+    if "f32" in res:
+        par["f32_output"] = res["f32"]
+        par["f32_output_stated_check"] = "pass" if fc.stated_ok(res["f32"]) else "fail"
+    return cpu, par
+
+
+def probe_ceilings(dev, stream) -> dict:
+    """Sustained matrix-core rate (bf16 32x32x16 products, random operands, two waves per
+    SIMD) and HBM read bandwidth (non-temporal 16-byte loads over 2 GiB) on this chip."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "io_aware_exact_21_amd", "libfa_probe.so"))
+    lib.fa_probe_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.fa_probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                      ctypes.c_void_p]
+    sp = stream.cuda_stream
+    blocks, iters = 1024, 400
+    ops = torch.randn(blocks * 512 * 10 * 8, device=dev).to(torch.bfloat16)
+    sink = torch.empty(blocks * 512, dtype=torch.float32, device=dev)
+
+    def timed(fn, n):
+        for _ in range(n):                      # as many untimed launches first (sustained clock)
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    def mfma():
+        if lib.fa_probe_mfma_bf16(ops.data_ptr(), sink.data_ptr(), blocks, iters, sp) != 0:
+            raise RuntimeError("fa_probe_mfma_bf16 failed")
+    ms = timed(mfma, 20)
+    mfma_tf = blocks * 8 * iters * 8 * 32768.0 / (ms * 1e-3) / 1e12
+    nbytes = 2 << 30
+    buf = torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device=dev)
+    rblocks = 512
+
+    def read():
+        if lib.fa_probe_hbm_read(buf.data_ptr(), nbytes, sink.data_ptr(), rblocks, sp) != 0:
+            raise RuntimeError("fa_probe_hbm_read failed")
+    ms_r = timed(read, 10)
+    gbs = nbytes / (ms_r * 1e-3) / 1e9
+    del buf, ops
+    return {"mfma_bf16": {"value": round(mfma_tf, 1), "unit": "TFLOP/s", "frac_of_spec": round(mfma_tf / PEAK_MFMA_BF16_TFLOPS, 4),
+                          "probe": "fa_probe_mfma_bf16: 1024 workgroups x 8 waves (one workgroup per CU), 400 "
+                                   "rounds of 8 v_mfma_f32_32x32x16_bf16 on random operands held in registers"},
+            "hbm_read": {"value": round(gbs, 1), "unit": "GB/s", "frac_of_spec": round(gbs / PEAK_HBM_GBS, 4),
+                         "probe": "fa_probe_hbm_read: 2 GiB, 512 workgroups x 128 threads, each streaming its "
+                                  "own 4 MiB slice with non-temporal 16-byte loads, 8 in flight per thread"}}
+
+
+def time_calls(stream, call, steps: int, warmup: int) -> float:
+    """Average ms of ``call`` over ``steps`` back-to-back calls after ``warmup`` calls (HIP events)."""
+    import torch
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def prefill_bench(fa, lib, stream, key: str, w, up, steps: int, warmup: int) -> tuple:
+    """One more prefill workload through fa_fwd, timed on its own; returns its JSON object
+    and the inputs and outputs the oracle leg compares."""
+    import torch
+    from synth import make_workload
+    print(f"[bench] prefill workload {w.name}", file=sys.stderr, flush=True)
+    q, k, v = make_workload(w)
+    tq, tk, tv = up(q), up(k), up(v)
+    o = torch.empty_like(tq)
+    lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=tq.device)
+    sp = stream.cuda_stream
+
+    def call():
+        fa._lib.check(lib.fa_fwd(tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                 w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.d, int(w.causal), w.scale, sp), "fa_fwd")
+    ms = time_calls(stream, call, steps, warmup)
+    flops = fwd_flops(w)
+    tflops = flops / (ms * 1e-3) / 1e12
+    o32, l32 = fa.fwd(tq, tk, tv, causal=w.causal, scale=w.scale, out_f32=True)
+    torch.cuda.synchronize()
+    outs = {"bf16": (o.float().cpu().numpy(), lse.cpu().numpy()), "f32": (o32.cpu().numpy(), l32.cpu().numpy())}
+    rec = {"config": {**w.describe(), "scale": w.scale, "seed": w.seed},
+           "value": round(tflops, 2), "unit": "TFLOP/s", "ms": round(ms, 4),
+           "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_BF16_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_BF16_TFLOPS, 4),
+                        "traffic": measured_traffic(f"fa_fwd_{key}_hbm_traffic.txt", "fwd"),
+                        "kernel": "fa_fwd_kernel", "avg_kernel_ms": round(ms, 4), "algorithmic_flops": flops,
+                        "algorithmic_bytes": fwd_bytes(w)},
+           "note": "fa_fwd timed with HIP events around back-to-back calls on the library's stream"}
+    return rec, (q, k, v, outs)
 
 
 def paged_decode_bench(fa, dev, stream, steps: int, warmup: int) -> dict:
@@ -330,12 +442,14 @@ def main() -> int:
     # so the bench runs two chunks per sequence; at this batch (B 64, Hkv 8) the library's
     # own default (0 below) picks one chunk, since 512 unsplit workgroups already fill the chip.
     ap.add_argument("--num-splits", type=int, default=2, help="decode KV splits (0 = library heuristic)")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle CPU time")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle leg (CPU baseline and stated-check parity per workload)")
+    ap.add_argument("--no-other-prefill", action="store_true", help="skip the other prefill workloads")
     ap.add_argument("--no-paged", action="store_true", help="skip the paged-cache decode measurement")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward measurement")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 forward measurement")
     ap.add_argument("--no-bpt", action="store_true", help="skip the blockwise attention + FFN measurement")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the ceiling probes")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run plain device copies of MIB MiB (reference reading for the HBM byte counters)")
     args = ap.parse_args()
@@ -347,6 +461,12 @@ def main() -> int:
 
     import numpy as np
     import torch
+
+    oracle_on = not args.no_cpu_baseline and args.copy_calibration == 0
+    if oracle_on:
+        # the oracle's worker processes are spawned before this process touches the GPU
+        from oracle import fullcheck
+        fullcheck.start_pool()
 
     import io_aware_exact_21_amd as fa
     from synth import WORKLOADS, make_workload
@@ -374,7 +494,8 @@ def main() -> int:
     tq, tk, tv = up(qf), up(kf), up(vf)
     qd, kd, vd = make_workload(wd)
     dq, dk, dv = up(qd), up(kd), up(vd)
-    del kd, vd
+    if not oracle_on:
+        del kd, vd
     ns = args.num_splits if args.num_splits > 0 else fa.decode_default_splits(wd.B, wd.Hkv, wd.Skv, wd.d)
     o = torch.empty_like(tq)
     lse = torch.empty((wf.B, wf.Hq, wf.Sq), dtype=torch.float32, device=dev)
@@ -429,6 +550,16 @@ def main() -> int:
     dec_gbs = db["total"] / ((split_ms + comb_ms) * 1e-3) / 1e9
     split_gbs = db["split_kernel"] / (split_ms * 1e-3) / 1e9
 
+    # outputs of the timed calls, for the oracle leg (the forward also once with fp32 output)
+    outputs = {}
+    if oracle_on:
+        o32, l32 = fa.fwd(tq, tk, tv, causal=wf.causal, scale=wf.scale, out_f32=True)
+        torch.cuda.synchronize()
+        outputs[args.fwd_workload] = (wf, (qf, kf, vf), {"bf16": (o.float().cpu().numpy(), lse.cpu().numpy()),
+                                                         "f32": (o32.cpu().numpy(), l32.cpu().numpy())})
+        del o32, l32
+        outputs["decode"] = (wd, (qd, kd, vd), {"bf16": (od.float().cpu().numpy(), ld.cpu().numpy())})
+
     t_fwd = measured_traffic(f"fa_fwd_{args.fwd_workload}_hbm_traffic.txt", "fwd")
     t_dec = measured_traffic("fa_decode_split_decode_hbm_traffic.txt", "decode")
     rec = {
@@ -454,6 +585,25 @@ def main() -> int:
         "wall_s_timed": round(t_wall, 3),
         "kernel_source_hash": {f: kernel_source_hash(f) for f in KERNEL_SOURCES},
     }
+    if not args.no_other_prefill:
+        rec["prefill_other"] = {}
+        for key in ("mha2k", "gqa32k"):
+            if key == args.fwd_workload:
+                continue
+            sub, data = prefill_bench(fa, lib, stream, key, WORKLOADS[key], up, args.steps, args.warmup)
+            rec["prefill_other"][key] = sub
+            if oracle_on:
+                outputs[key] = (WORKLOADS[key], data[:3], data[3])
+            del data
+    if oracle_on and args.fwd_workload != "tiny":
+        # the tiny exact-check workload is a parity case only: one call, no timing
+        wt = WORKLOADS["tiny"]
+        qt, kt, vt = make_workload(wt)
+        ot, lt = fa.fwd(up(qt), up(kt), up(vt), causal=wt.causal, scale=wt.scale)
+        ot32, lt32 = fa.fwd(up(qt), up(kt), up(vt), causal=wt.causal, scale=wt.scale, out_f32=True)
+        torch.cuda.synchronize()
+        outputs["tiny"] = (wt, (qt, kt, vt), {"bf16": (ot.float().cpu().numpy(), lt.cpu().numpy()),
+                                              "f32": (ot32.cpu().numpy(), lt32.cpu().numpy())})
     if not args.no_bwd:
         rec["backward"] = backward_bench(fa, lib, stream, args.fwd_workload, wf, tq, tk, tv, o, lse, args.steps,
                                          args.warmup)
@@ -463,12 +613,31 @@ def main() -> int:
         rec["fp8_forward"] = fp8_bench(fa, stream, args.fwd_workload, wf, args.steps, args.warmup)
     if not args.no_paged:
         rec["paged_decode"] = paged_decode_bench(fa, dev, stream, args.steps, args.warmup)
+    del tq, tk, tv, dq, dk, dv
+    if not args.no_ceilings:
+        print("[bench] ceiling probes", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+        ceil = probe_ceilings(dev, stream)
+        rec["ceilings"] = ceil
+        rec["roofline"]["frac_of_measured_ceiling"] = round(tflops / ceil["mfma_bf16"]["value"], 4)
+        rec["decode"]["roofline"]["frac_of_measured_ceiling"] = round(split_gbs / ceil["hbm_read"]["value"], 4)
+        for sub in rec.get("prefill_other", {}).values():
+            sub["roofline"]["frac_of_measured_ceiling"] = round(sub["value"] / ceil["mfma_bf16"]["value"], 4)
 
-    if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(wf, qf, kf, vf, args.cpu_budget)
-    else:
-        rec["cpu_baseline"] = None
+    rec["cpu_baseline"] = None
+    if oracle_on:
+        rec["parity"] = {}
+        for key, (w, (q, k, v), outs) in outputs.items():
+            print(f"[bench] oracle leg: {w.name}", file=sys.stderr, flush=True)
+            cpu, par = oracle_leg(key, w, q, k, v, outs)
+            if key == args.fwd_workload:
+                rec["cpu_baseline"], rec["parity"] = cpu, par
+            elif key == "decode":
+                rec["decode"]["cpu_baseline"], rec["decode"]["parity"] = cpu, par
+            elif key in rec.get("prefill_other", {}):
+                rec["prefill_other"][key]["cpu_baseline"], rec["prefill_other"][key]["parity"] = cpu, par
+            else:
+                rec["parity_only"] = {"config": {**w.describe(), "seed": w.seed}, "parity": par}
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -15,6 +15,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
+# ceiling probes (sustained matrix-core rate, HBM read bandwidth): a separate library
+PROBE_LIB = os.path.join(PKG, "libfa_probe.so")
+PROBE_SOURCES = ["fa_probe.hip"]
 SOURCES = ["fa_fwd.hip", "fa_decode.hip", "fa_bwd.hip", "fa_fwd_fp8.hip", "fa_bpt.hip", "fa_api.hip"]
 # The kernel sources assume finite inputs (non-finite Q/K/V are unsupported), which
 # lets the compiler drop NaN canonicalisation around the softmax max. The C ABI source
@@ -22,6 +25,8 @@ SOURCES = ["fa_fwd.hip", "fa_decode.hip", "fa_bwd.hip", "fa_fwd_fp8.hip", "fa_bp
 KERNEL_ONLY_FLAGS = {"fa_fwd.hip": ["-fno-honor-nans"], "fa_decode.hip": ["-fno-honor-nans"],
                      "fa_fwd_fp8.hip": ["-fno-honor-nans"]}
 ARCH = "gfx950"
+# libraries the attention library links besides the HIP runtime
+EXTRA_LIBS = ["-lhipblaslt"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
@@ -51,9 +56,10 @@ def build(verbose: bool = False) -> str:
     hipcc = _hipcc()
     os.makedirs(BUILD, exist_ok=True)
     objs, cmds = [], []
-    for src in SOURCES:
+    for src in SOURCES + PROBE_SOURCES:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-        objs.append(obj)
+        if src in SOURCES:
+            objs.append(obj)
         cmds.append([hipcc, *HIPCC_FLAGS, *KERNEL_ONLY_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(len(cmds)) as ex:
         for out in ex.map(_run, cmds):
@@ -61,8 +67,11 @@ def build(verbose: bool = False) -> str:
                 print(out)
     tmp = LIB + ".tmp"
     # hipBLASLt runs the feed-forward GEMMs of the blockwise transformer layer
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp, "-lhipblaslt"])
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp, *EXTRA_LIBS])
     os.replace(tmp, LIB)
+    probe_objs = [os.path.join(BUILD, src.replace(".hip", ".o")) for src in PROBE_SOURCES]
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *probe_objs, "-o", PROBE_LIB + ".tmp"])
+    os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
     return LIB
 
 
