@@ -37,6 +37,10 @@ int check_common(int B, int Hq, int Hkv, int Sq, int Skv, int d) {
   return FA_OK;
 }
 
+// The streaming kernels address the rows of one tile with 32-bit per-lane byte offsets
+// from the tile's first row: `rows` rows of `row_bytes` each must span less than 2^32 bytes.
+bool tile_offsets_fit(int rows, double row_bytes) { return (double)rows * row_bytes <= 4294967296.0; }
+
 // The kernels need a positive exponent factor c = |scale| * log2(e). A negative scale
 // is folded into Q by flipping its sign bits (exact in bf16). With scale == 0 every
 // score is exactly 0, which is what a zeroed Q gives for any c, so Q is masked to 0.
@@ -54,6 +58,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
   int st = check_common(B, Hq, Hkv, Sq, Skv, d);
   if (st != FA_OK) return st;
   if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
+  if (!tile_offsets_fit(64, (double)Hkv * d * 2)) return FA_ERR_SHAPE;   // 64-key K/V tiles
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)))
     return FA_ERR_ALIGN;
   fa::FwdParams p;
@@ -344,6 +349,8 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
   if (st != FA_OK) return st;
   if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
   if (!isfinite(scale)) return FA_ERR_SHAPE;
+  // 64-row K/V tiles (dQ kernel) and 128-row Q/dO tiles (dK/dV kernel)
+  if (!tile_offsets_fit(64, (double)Hkv * d * 2) || !tile_offsets_fit(128, (double)Hq * d * 2)) return FA_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
       !aligned16(dk) || !aligned16(dv) || !aligned16(lse))
     return FA_ERR_ALIGN;
@@ -381,6 +388,7 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* vt8, const float* q_s
   // that d rows of one head stay within 32-bit byte offsets
   if (ldv % 16 != 0 || ldv < (Skv + 15) / 16 * 16 || (double)ldv * d > 2.0e9) return FA_ERR_SHAPE;
   if ((double)B * Hkv * d * ldv > 4.0e18) return FA_ERR_SHAPE;
+  if (!tile_offsets_fit(64, (double)Hkv * d)) return FA_ERR_SHAPE;        // 64-key e4m3 K tiles
   if (!aligned16(q8) || !aligned16(k8) || !aligned16(vt8) || !aligned16(o) || (lse && !aligned16(lse)))
     return FA_ERR_ALIGN;
   if ((reinterpret_cast<uintptr_t>(q_scale) | reinterpret_cast<uintptr_t>(k_scale) |
@@ -415,6 +423,7 @@ int fa_bpt_layer(const void* q, const void* k, const void* v, const void* w1, co
   int st = check_common(B, Hq, Hkv, S, S, d);
   if (st != FA_OK) return st;
   if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
+  if (!tile_offsets_fit(64, (double)Hkv * d * 2)) return FA_ERR_SHAPE;
   if (d_ff < 1 || block_rows < 1 || (double)Hq * d * d_ff > 2.0e9 || (double)B * S * Hq * d > 4.0e18)
     return FA_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(w1) || !aligned16(b1) || !aligned16(w2) ||

@@ -248,3 +248,19 @@ def test_decode_noalloc_validation(lib):
     limit = 16 << 20
     assert lib.fa_decode_workspace_bytes(64, 32, 128, 40) > limit
     assert dec(B=64, Hq=32, Hkv=8, Skv=64 * 40, ns=40) == FA_ERR_WORKSPACE
+
+
+def test_tile_offsets_must_fit_32_bits(lib):
+    """The streaming kernels address a tile's rows with 32-bit byte offsets from its first
+    row: shapes whose 64-key K/V tiles (128-row Q/dO tiles in the backward) span 2^32 bytes
+    or more are refused before launching."""
+    from io_aware_exact_21_amd._lib import FA_ERR_SHAPE
+    ok_heads = (1 << 32) // (64 * 128 * 2)                  # 262144 KV heads of d = 128: exactly 2^32
+    assert _fwd(lib, Hq=ok_heads + 1, Hkv=ok_heads + 1, d=128, Sq=2, Skv=2) == FA_ERR_SHAPE
+    assert _fwd(lib, Hq=ok_heads, Hkv=ok_heads, d=128, Sq=2, Skv=2, q=A + 8) != FA_ERR_SHAPE   # fits: align error next
+    assert lib.fa_fwd_f32out(A, A, A, A, None, 1, 2 * ok_heads + 1, 2 * ok_heads + 1, 2, 2, 64, 0, 1.0, None) == FA_ERR_SHAPE
+    # backward: 128-row Q/dO tiles bound the query heads, 64-row K/V tiles the KV heads
+    hq = (1 << 32) // (128 * 128 * 2) + 1
+    assert lib.fa_bwd(A, A, A, A, A, A, A, A, A, 1, hq, 1, 2, 2, 128, 0, 0.1, A, 1 << 20, None) == FA_ERR_SHAPE
+    n8 = (1 << 20) + 1                                         # 64 keys x n8 heads x 64 B > 2^32
+    assert lib.fa_fwd_fp8(A, A, A, A, A, A, A, None, 1, n8, n8, 2, 2, 16, 64, 0, 0.1, None) == FA_ERR_SHAPE
