@@ -15,23 +15,28 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
 __device__ __forceinline__ const lds_u8* lds_ptr(unsigned a) { return (const lds_u8*)(uintptr_t)a; }
 
 // Wave-level copies: lane i's 16 (copy16) or 4 (copy4) bytes at base + voff_i land at
-// LDS byte lds + 16 i (4 i); base is wave-uniform in SGPRs, the LDS destination goes in
-// m0, which the asm declares clobbered. Issued as inline assembly so the compiler does
-// not order later LDS reads of other ring stages behind it; completion is tracked with
-// wait_vmcnt plus a barrier.
+// LDS byte lds + 16 i (4 i); base is wave-uniform in SGPRs. The LDS destination travels
+// in m0, which the asm saves to a scratch SGPR first and restores after issuing the copy
+// (the instruction reads m0 when it issues), so m0 is unchanged for any code around it.
+// Issued as inline assembly so the compiler does not order later LDS reads of other ring
+// stages behind it; completion is tracked with wait_vmcnt plus a barrier.
 __device__ __forceinline__ void copy16(const void* base, unsigned voff, unsigned lds) {
   const unsigned m = __builtin_amdgcn_readfirstlane(lds);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(base), "s"(m)
-               : "memory", "m0");
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(base), "s"(m)
+      : "memory");
 }
 __device__ __forceinline__ void copy4(const void* base, unsigned voff, unsigned lds) {
   const unsigned m = __builtin_amdgcn_readfirstlane(lds);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
-               :
-               : "v"(voff), "s"(base), "s"(m)
-               : "memory", "m0");
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(base), "s"(m)
+      : "memory");
 }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
