@@ -395,7 +395,7 @@ def bpt_bench(fa, stream, w, tq, tk, tv, steps: int, warmup: int, block_rows: in
     flops = fwd_flops(w) + 4.0 * w.B * w.Sq * dm * dff
 
     def timed(rows):
-        nws = fa.bpt_workspace_bytes(min(rows, w.Sq), w.Hq, w.d, dff)
+        nws = fa.bpt_workspace_bytes(w.B, w.Sq, rows, w.Hq, w.d, dff)
         ws = torch.empty(nws, dtype=torch.uint8, device=dev)
 
         def call():
@@ -426,7 +426,7 @@ def bpt_bench(fa, stream, w, tq, tk, tv, steps: int, warmup: int, block_rows: in
                                         "workspace_bytes": nws_full},
             "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_BF16_TFLOPS, 4), "traffic": None,
-                         "kernel": "per block: fa_fwd_kernel + two hipBLASLt GEMMs", "algorithmic_flops": flops},
+                         "kernel": "per block of rows of every batch element: fa_fwd_kernel + two ffn_gemm_kernel", "algorithmic_flops": flops},
             "note": "fa_bpt_layer timed with HIP events around the call on the library's stream"}
 
 

@@ -259,37 +259,36 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* vt8, const float* q_s
                int causal, float scale, void* stream);
 
 /*
- * fa_bpt_workspace_bytes - device workspace fa_bpt_layer needs for blocks of
- * `block_rows` query rows: the block's attention output (bf16, block_rows x Hq*d),
- * its hidden activations (bf16, block_rows x d_ff), each rounded up to 256 bytes,
- * plus 32 MiB of GEMM scratch. 0 for bad sizes.
+ * fa_bpt_workspace_bytes - device workspace fa_bpt_layer needs: for one block of
+ * R = min(block_rows, S) query rows of every batch element, the block's attention output
+ * (bf16, B*R x Hq*d) and its hidden activations (bf16, B*R x d_ff), each rounded up to
+ * 256 bytes. 0 for bad sizes.
  */
-size_t fa_bpt_workspace_bytes(int block_rows, int Hq, int d, int d_ff);
+size_t fa_bpt_workspace_bytes(int B, int S, int block_rows, int Hq, int d, int d_ff);
 
 /*
  * fa_bpt_layer - attention followed by the position-wise feed-forward network, run
  * blockwise ("I/O-Aware Kernels", section Blockwise Parallel Transformers): for each
- * batch element and each block of `block_rows` query rows, the attention output of
- * the block (fa_fwd's kernel, causal positions taken from the whole sequence) goes
- * straight through
- *     y = relu(h W1 + b1) W2 + b2,   h = the block's attention output, heads concatenated,
- * so only one block's activations ever exist (the workspace), not the sequence's.
+ * block of `block_rows` query rows (taken from every batch element at once), the
+ * attention output of the block (fa_fwd's kernel, causal positions taken from the whole
+ * sequence) goes straight through
+ *     y = relu(h W1^T + b1) W2^T + b2,   h = the block's attention output, heads concatenated,
+ * so only one block's activations ever exist (the workspace), not the sequence's. Both
+ * products run on this library's bf16 matrix-core GEMM kernel (fp32 accumulation, the
+ * bias and ReLU applied to the fp32 sums, one bf16 rounding at the store).
  *
  *   q : bf16 [B, S, Hq, d];  k, v : bf16 [B, S, Hkv, d]  (self-attention, Sq = Skv = S)
- *   w1: bf16 [Hq*d, d_ff] row-major;  b1: bf16 [d_ff]
- *   w2: bf16 [d_ff, Hq*d] row-major;  b2: bf16 [Hq*d]
+ *   w1: bf16 [d_ff, Hq*d] (a linear layer's [out, in] weight);  b1: bf16 [d_ff]
+ *   w2: bf16 [Hq*d, d_ff];  b2: bf16 [Hq*d]
  *   y : bf16 [B, S, Hq*d]
- *   workspace: at least fa_bpt_workspace_bytes(min(block_rows, S), Hq, d, d_ff) bytes,
+ *   workspace: at least fa_bpt_workspace_bytes(B, S, block_rows, Hq, d, d_ff) bytes,
  *              256-byte aligned, caller-owned, overwritten.
- * The hidden activations are rounded to bf16 between the two GEMMs (fp32
- * accumulation in each). The GEMMs run on hipBLASLt with the bias and ReLU in its
- * epilogue; the library creates one hipBLASLt handle per device (the current device
- * of the calling thread) on first use, caches the GEMM plans per device and shape, and
- * serialises these calls with a lock. Same shape rules as fa_fwd; d_ff >= 1;
- * block_rows >= 1 (values >= S give the whole-sequence schedule). All tensors are
- * device memory, 16-byte aligned. Launches run on `stream` in order; nothing is
- * synchronised. Returns FA_OK or an FA_ERR_* code (FA_ERR_HIP for a launch or GEMM
- * failure, after earlier blocks may have run).
+ * The block's attention output and the hidden activations are rounded to bf16. Same
+ * shape rules as fa_fwd; d_ff a positive multiple of 64; block_rows >= 1 (values >= S
+ * give the whole-sequence schedule). All tensors are device memory, 16-byte aligned.
+ * Per block, three kernels run on `stream` in order; nothing is allocated or
+ * synchronised. Returns FA_OK or an FA_ERR_* code (FA_ERR_HIP for a failed launch, after
+ * earlier blocks may have run).
  */
 int fa_bpt_layer(const void* q, const void* k, const void* v, const void* w1, const void* b1, const void* w2,
                  const void* b2, void* y, int B, int Hq, int Hkv, int S, int d, int d_ff, int causal, float scale,

@@ -34,7 +34,7 @@ SIGNATURES = {
                                 c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_float,
                                 c_int, c_void_p, c_size_t, c_void_p]),
     "fa_bwd_workspace_bytes": (c_size_t, [c_int, c_int, c_int]),
-    "fa_bpt_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int]),
+    "fa_bpt_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int, c_int]),
     "fa_bpt_layer": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                              c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_float, c_int, c_void_p, c_size_t,
                              c_void_p]),

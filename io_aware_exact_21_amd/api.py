@@ -297,8 +297,8 @@ def fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, vt8: torch.Tensor, q_scale: torc
     return out, lse
 
 
-def bpt_workspace_bytes(block_rows: int, Hq: int, d: int, d_ff: int) -> int:
-    return int(_lib.load().fa_bpt_workspace_bytes(block_rows, Hq, d, d_ff))
+def bpt_workspace_bytes(B: int, S: int, block_rows: int, Hq: int, d: int, d_ff: int) -> int:
+    return int(_lib.load().fa_bpt_workspace_bytes(B, S, block_rows, Hq, d, d_ff))
 
 
 def bpt_layer(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w1: torch.Tensor, b1: torch.Tensor,
@@ -306,8 +306,8 @@ def bpt_layer(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w1: torch.Tenso
               workspace: torch.Tensor | None = None, out: torch.Tensor | None = None):
     """Attention + feed-forward network, blockwise (see fa_bpt_layer in include/fa.h).
 
-    q [B,S,Hq,d], k/v [B,S,Hkv,d], w1 [Hq*d, d_ff], b1 [d_ff], w2 [d_ff, Hq*d], b2 [Hq*d], all
-    bf16 -> y bf16 [B, S, Hq*d].
+    q [B,S,Hq,d], k/v [B,S,Hkv,d], w1 [d_ff, Hq*d], b1 [d_ff], w2 [Hq*d, d_ff], b2 [Hq*d]
+    (linear-layer [out, in] weights), all bf16 -> y bf16 [B, S, Hq*d].
     """
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n, torch.bfloat16, 4)
@@ -320,12 +320,11 @@ def bpt_layer(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w1: torch.Tenso
     _need(w2, "w2", torch.bfloat16, 2)
     _need(b1, "b1", torch.bfloat16, 1)
     _need(b2, "b2", torch.bfloat16, 1)
-    d_ff = w1.shape[1]
-    if tuple(w1.shape) != (dm, d_ff) or tuple(w2.shape) != (d_ff, dm) or tuple(b1.shape) != (d_ff,) \
+    d_ff = w1.shape[0]
+    if tuple(w1.shape) != (d_ff, dm) or tuple(w2.shape) != (dm, d_ff) or tuple(b1.shape) != (d_ff,) \
             or tuple(b2.shape) != (dm,):
         raise ValueError("feed-forward weights do not match d_model = Hq * d")
-    rows = min(block_rows, S)
-    need = bpt_workspace_bytes(rows, Hq, d, d_ff)
+    need = bpt_workspace_bytes(B, S, block_rows, Hq, d, d_ff)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if out is None:

@@ -89,13 +89,14 @@ int main() {
   EXPECT(fa_fwd_fp8(A, A, A, F2, F, F, A, nullptr, 2, 8, 2, 100, 90, 96, 128, 1, 0.1f, nullptr), FA_ERR_ALIGN);
   EXPECT(fa_fwd_fp8(A, A, A, F, F, F, A, nullptr, 1, 1048577, 1048577, 2, 2, 16, 64, 0, 0.1f, nullptr), FA_ERR_SHAPE);
   // ---- blockwise layer
-  const size_t pneed = fa_bpt_workspace_bytes(64, 4, 64, 1024);
+  const size_t pneed = fa_bpt_workspace_bytes(2, 100, 64, 4, 64, 1024);
   EXPECT(fa_bpt_layer(A, A, A, A, A, A, A, A, 2, 4, 2, 100, 64, 1024, 1, 0.1f, 128, A, pneed, nullptr),
          FA_ERR_WORKSPACE);
   EXPECT(fa_bpt_layer(A, A, A, A, A, A, A, A, 2, 4, 2, 100, 64, 0, 1, 0.1f, 64, A, pneed, nullptr), FA_ERR_SHAPE);
   EXPECT(fa_bpt_layer(A, A, A, A, A, A, A, A, 2, 4, 2, 100, 64, 1024, 1, 0.1f, 64, A8, pneed, nullptr),
          FA_ERR_ALIGN);
-  EXPECT((int)(fa_bpt_workspace_bytes(0, 4, 64, 1024) == 0), 1);
+  EXPECT((int)(fa_bpt_workspace_bytes(0, 100, 64, 4, 64, 1024) == 0), 1);
+  EXPECT(fa_bpt_layer(A, A, A, A, A, A, A, A, 2, 4, 2, 100, 64, 1000, 1, 0.1f, 64, A, pneed, nullptr), FA_ERR_SHAPE);
   // ---- status strings
   for (int st = -3; st < 10; ++st) EXPECT((int)(fa_status_string(st) != nullptr), 1);
   if (failures) {

@@ -68,6 +68,8 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
   p.o = o;
   p.lse = lse;
   p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Sq = Sq; p.Skv = Skv; p.d = d;
+  p.q_bstride = p.o_bstride = (int64_t)Sq * Hq * d;
+  p.kv_bstride = (int64_t)Skv * Hkv * d;
   st = scale_terms(scale, &p.c, &p.qsign, &p.qmask);
   if (st != FA_OK) return st;
   if (fa::fwd_grid_size(B, Hq, Sq, d) > 0x7fffffffLL) return FA_ERR_SHAPE;
@@ -411,9 +413,10 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* vt8, const float* q_s
   return FA_OK;
 }
 
-size_t fa_bpt_workspace_bytes(int block_rows, int Hq, int d, int d_ff) {
-  if (block_rows < 1 || Hq < 1 || d < 1 || d_ff < 1) return 0;
-  return align256((size_t)block_rows * Hq * d * 2) + align256((size_t)block_rows * d_ff * 2) + fa::kBptGemmWorkspace;
+size_t fa_bpt_workspace_bytes(int B, int S, int block_rows, int Hq, int d, int d_ff) {
+  if (B < 1 || S < 1 || block_rows < 1 || Hq < 1 || d < 1 || d_ff < 1) return 0;
+  const size_t rows = (size_t)B * (block_rows < S ? block_rows : S);
+  return align256(rows * Hq * d * 2) + align256(rows * d_ff * 2);
 }
 
 int fa_bpt_layer(const void* q, const void* k, const void* v, const void* w1, const void* b1, const void* w2,
@@ -424,45 +427,58 @@ int fa_bpt_layer(const void* q, const void* k, const void* v, const void* w1, co
   if (st != FA_OK) return st;
   if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
   if (!tile_offsets_fit(64, (double)Hkv * d * 2)) return FA_ERR_SHAPE;
-  if (d_ff < 1 || block_rows < 1 || (double)Hq * d * d_ff > 2.0e9 || (double)B * S * Hq * d > 4.0e18)
+  // the GEMMs take K in steps of 64 and N in blocks of 32, and address a 256-row tile with
+  // 32-bit offsets (d_model = Hq * d is a multiple of 64 already)
+  if (d_ff < 64 || d_ff % 64 != 0 || block_rows < 1 || (double)Hq * d * d_ff > 2.0e9 ||
+      (double)B * S * Hq * d > 4.0e18 || !tile_offsets_fit(256, (double)d_ff * 2) ||
+      !tile_offsets_fit(256, (double)Hq * d * 2))
     return FA_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(w1) || !aligned16(b1) || !aligned16(w2) ||
       !aligned16(b2) || !aligned16(y))
     return FA_ERR_ALIGN;
   const int rows_max = block_rows < S ? block_rows : S;
-  if (fa::fwd_grid_size(1, Hq, rows_max, d) > 0x7fffffffLL) return FA_ERR_SHAPE;
-  if (!workspace || workspace_bytes < fa_bpt_workspace_bytes(rows_max, Hq, d, d_ff)) return FA_ERR_WORKSPACE;
+  // one block of rows of every batch element runs at once
+  if ((double)B * rows_max > 2.0e9 || fa::fwd_grid_size(B, Hq, rows_max, d) > 0x7fffffffLL ||
+      fa::ffn_gemm_grid(B * rows_max, d_ff) > 0x7fffffffLL)
+    return FA_ERR_SHAPE;
+  if (!workspace || workspace_bytes < fa_bpt_workspace_bytes(B, S, block_rows, Hq, d, d_ff)) return FA_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return FA_ERR_ALIGN;
   fa::FwdParams p;
-  p.k = nullptr;
   st = scale_terms(scale, &p.c, &p.qsign, &p.qmask);
   if (st != FA_OK) return st;
-  // workspace: attention output of one block [rows, Hq*d], its hidden activations
-  // [rows, d_ff], then the GEMM scratch
+  // workspace: the attention output of one row block of every batch element
+  // [B * rows, Hq * d], then its hidden activations [B * rows, d_ff]
   const int dm = Hq * d;
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   uint16_t* attn = reinterpret_cast<uint16_t*>(ws);
-  uint16_t* mid = reinterpret_cast<uint16_t*>(ws + align256((size_t)rows_max * dm * 2));
-  void* gws = ws + align256((size_t)rows_max * dm * 2) + align256((size_t)rows_max * d_ff * 2);
+  uint16_t* mid = reinterpret_cast<uint16_t*>(ws + align256((size_t)B * rows_max * dm * 2));
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  for (int b = 0; b < B; ++b) {
-    for (int r0 = 0; r0 < S; r0 += rows_max) {
-      const int rows = S - r0 < rows_max ? S - r0 : rows_max;
-      // attention of the block's query rows: causal rows r0.. see keys up to their own
-      // position, which the bottom-right alignment gives with Skv = r0 + rows
-      p.q = static_cast<const uint16_t*>(q) + ((int64_t)b * S + r0) * Hq * d;
-      p.k = static_cast<const uint16_t*>(k) + (int64_t)b * S * Hkv * d;
-      p.v = static_cast<const uint16_t*>(v) + (int64_t)b * S * Hkv * d;
-      p.o = attn;
-      p.lse = nullptr;
-      p.B = 1; p.Hq = Hq; p.Hkv = Hkv; p.Sq = rows; p.Skv = causal ? r0 + rows : S; p.d = d;
-      if (fa::launch_fwd(p, causal != 0, false, hs) != hipSuccess) return FA_ERR_HIP;
-      // feed-forward network of the block: relu(attn W1 + b1) W2 + b2
-      if (fa::ffn_gemm(rows, d_ff, dm, attn, w1, b1, mid, true, gws, fa::kBptGemmWorkspace, hs)) return FA_ERR_HIP;
-      uint16_t* yb = static_cast<uint16_t*>(y) + ((int64_t)b * S + r0) * dm;
-      if (fa::ffn_gemm(rows, dm, d_ff, mid, w2, b2, yb, false, gws, fa::kBptGemmWorkspace, hs)) return FA_ERR_HIP;
-    }
+  for (int r0 = 0; r0 < S; r0 += rows_max) {
+    const int rows = S - r0 < rows_max ? S - r0 : rows_max;
+    // attention of query rows r0 .. r0 + rows - 1 of every batch element: causal rows see
+    // keys up to their own position, which the bottom-right alignment gives with
+    // Skv = r0 + rows; q and k/v keep the whole sequence's batch strides
+    p.q = static_cast<const uint16_t*>(q) + (int64_t)r0 * dm;
+    p.k = static_cast<const uint16_t*>(k);
+    p.v = static_cast<const uint16_t*>(v);
+    p.o = attn;
+    p.lse = nullptr;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Sq = rows; p.Skv = causal ? r0 + rows : S; p.d = d;
+    p.q_bstride = (int64_t)S * dm;
+    p.kv_bstride = (int64_t)S * Hkv * d;
+    p.o_bstride = (int64_t)rows * dm;
+    if (fa::launch_fwd(p, causal != 0, false, hs) != hipSuccess) return FA_ERR_HIP;
+    // feed-forward network of the block: mid = relu(attn W1^T + b1), y = mid W2^T + b2
+    fa::FfnGemmParams g1;
+    g1.x = attn; g1.w = static_cast<const uint16_t*>(w1); g1.bias = static_cast<const uint16_t*>(b1); g1.c = mid;
+    g1.M = B * rows; g1.N = d_ff; g1.K = dm; g1.ldc = d_ff; g1.group_rows = g1.M; g1.group_stride = g1.M;
+    if (fa::launch_ffn_gemm(g1, true, hs) != hipSuccess) return FA_ERR_HIP;
+    fa::FfnGemmParams g2;
+    g2.x = mid; g2.w = static_cast<const uint16_t*>(w2); g2.bias = static_cast<const uint16_t*>(b2);
+    g2.c = static_cast<uint16_t*>(y) + (int64_t)r0 * dm;          // row b * rows + i -> y[b, r0 + i]
+    g2.M = B * rows; g2.N = dm; g2.K = d_ff; g2.ldc = dm; g2.group_rows = rows; g2.group_stride = S;
+    if (fa::launch_ffn_gemm(g2, false, hs) != hipSuccess) return FA_ERR_HIP;
   }
   return FA_OK;
 }

@@ -2,18 +2,28 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
-#include <stddef.h>
+#include <stdint.h>
 
 namespace fa {
 
-// Bytes of device workspace one FFN GEMM may use (hipBLASLt's own scratch).
-constexpr size_t kBptGemmWorkspace = size_t(32) << 20;
+// C[map(m), n] = act(sum_k x[m, k] w[n, k] + bias[n]) for m < M, n < N; bf16 in and out,
+// fp32 accumulation, act = ReLU or identity. x [M, K] and w [N, K] are row-major (k
+// contiguous; w is a linear layer's [out, in] weight). Output row m goes to row
+// map(m) = (m / group_rows) * group_stride + m % group_rows of c, rows ldc elements
+// apart. Requirements (checked by the caller): K a multiple of 64, N a multiple of 32,
+// 255 * K * 2 < 2^32, pointers 16-byte aligned, ldc a multiple of 4.
+struct FfnGemmParams {
+  const uint16_t* x;
+  const uint16_t* w;
+  const uint16_t* bias;
+  uint16_t* c;
+  int M, N, K;
+  int64_t ldc;
+  int group_rows;
+  int64_t group_stride;
+};
 
-// Row-major D [M, N] = X [M, K] W [K, N] + bias [N], then ReLU if `relu`; bf16 in and out,
-// fp32 accumulation (hipBLASLt, with the bias and ReLU in its epilogue). Returns 0 on
-// success, a hipBLASLt status otherwise. Serialised by a process-wide lock; the
-// hipBLASLt handle and per-shape plans are created on first use and kept.
-int ffn_gemm(int M, int N, int K, const void* x, const void* w, const void* bias, void* d, bool relu,
-             void* workspace, size_t workspace_bytes, hipStream_t stream);
+long long ffn_gemm_grid(int M, int N);
+hipError_t launch_ffn_gemm(const FfnGemmParams& p, bool relu, hipStream_t stream);
 
 }  // namespace fa

@@ -1,0 +1,223 @@
+// Feed-forward GEMMs of the blockwise transformer layer on the bf16 matrix cores.
+//
+// The feed-forward network acts on every token on its own ("I/O-Aware Kernels", section
+// Blockwise Parallel Transformers), so each of its two products is a dense GEMM over the
+// rows of one query block:  C[m, n] = act(sum_k X[m, k] W[n, k] + bias[n]),
+// with X the block's activations [M, K] and W a linear layer's weights [N, K] (both
+// row-major, k contiguous), fp32 accumulation, the bias and the optional ReLU applied
+// to the fp32 sum, and one bf16 rounding (round-to-nearest-even) at the store.
+//
+// One workgroup of eight waves (two per SIMD) computes a 256 x 256 tile of C. Tiles of
+// kBK k-columns of X and W stream through an LDS ring of kStages stages by direct
+// global -> LDS copies, issued kStages - 1 stages ahead. The products are formed transposed, C^T = W X^T, on
+// v_mfma_f32_32x32x16_bf16: the W rows are the A operand and the X rows the B operand,
+// so in the accumulator a lane owns one row m of C and 4 consecutive n per register
+// group, which makes the bf16 stores 8 bytes wide. Each wave owns 64 rows m x 128
+// columns n (2 x 4 products per 16-wide k step, every LDS operand read feeding two or
+// four products).
+#include "fa_bpt.hpp"
+#include "fa_device.hpp"
+#include "fa_dma.hpp"
+
+namespace fa {
+
+namespace {
+
+#ifndef FA_FFN_BK
+#define FA_FFN_BK 64
+#endif
+#ifndef FA_FFN_STAGES
+#define FA_FFN_STAGES 2
+#endif
+constexpr int kBM = 256, kBN = 256;
+constexpr int kBK = FA_FFN_BK;                     // k columns per LDS stage
+constexpr int kStages = FA_FFN_STAGES;             // LDS ring depth
+constexpr int kWaves = 8;                          // 4 along m x 2 along n
+constexpr int kRowBytes = kBK * 2;                 // bytes per tile row
+constexpr int kChunks = kRowBytes / 16;            // 16-byte chunks per tile row
+constexpr int kRowsPerCopy = 1024 / kRowBytes;     // tile rows per wave-level copy (1 KiB)
+constexpr int kCopiesPerWave = kBM / kRowsPerCopy / kWaves;   // per tile and wave
+constexpr unsigned kTileBytes = kBM * kRowBytes;   // X tile; the W tile is the same size
+constexpr unsigned kStageBytes = 2 * kTileBytes;
+constexpr int kSwzShift = kChunks == 8 ? 1 : 2;    // rows per 256-byte bank window: 2 or 4
+static_assert(kBK == 32 || kBK == 64, "tile depth");
+static_assert(kStages * kStageBytes <= 160 * 1024, "LDS ring");
+
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
+// 16-byte chunk c of tile row r sits at chunk c ^ swz(r): sixteen consecutive rows read at
+// one logical chunk then fall on sixteen distinct 16-byte bank groups of the 256-byte bank
+// window (a row is half or a quarter of that window).
+__device__ __forceinline__ int ffn_swz(int r) { return (r >> kSwzShift) & (kChunks - 1); }
+
+// Per-lane byte offsets of the wave-level copies of one 256-row tile: copy i fills tile
+// rows kRowsPerCopy i ...; lane l takes row kRowsPerCopy i + l / kChunks and fetches its
+// global chunk (l % kChunks) ^ swz(row). Rows at or past `rows` (the ragged edge of the
+// matrix) re-read the last row; their results are never stored.
+struct TileCopy {
+  unsigned off[kCopiesPerWave];
+
+  __device__ __forceinline__ void init(int64_t row_stride_bytes, int rows, int w, int lane) {
+#pragma unroll
+    for (int j = 0; j < kCopiesPerWave; ++j) {
+      const int r = kRowsPerCopy * (w + kWaves * j) + lane / kChunks;
+      const int rg = min(r, rows - 1);
+      off[j] = (unsigned)(rg * row_stride_bytes) + (unsigned)(((lane % kChunks) ^ ffn_swz(r)) << 4);
+    }
+  }
+  __device__ __forceinline__ void issue(const void* base, unsigned lds, int w) const {
+#pragma unroll
+    for (int j = 0; j < kCopiesPerWave; ++j) dma::copy16(base, off[j], lds + (w + kWaves * j) * 1024);
+  }
+};
+
+// Operands of one 16-wide k step: four 32-row W blocks (A operands) and two 32-row X
+// blocks (B operands) of this wave, at per-lane offset `off` within their 32-row blocks.
+__device__ __forceinline__ void load_step(unsigned wbase, unsigned xbase, unsigned off, u32x4 (&a)[4],
+                                          u32x4 (&b)[2]) {
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+    a[nb] = *reinterpret_cast<const lds_u32x4*>(dma::lds_ptr(wbase + off) + nb * 32 * kRowBytes);
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+    b[mb] = *reinterpret_cast<const lds_u32x4*>(dma::lds_ptr(xbase + off) + mb * 32 * kRowBytes);
+}
+
+template <bool RELU>
+__global__ __launch_bounds__(kWaves * 64, 1) void ffn_gemm_kernel(FfnGemmParams p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages * kStageBytes];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w & 3, wn = w >> 2;               // wave position: 64-row slab m, 128-column slab n
+
+  // ---- tile of this workgroup: workgroups are dealt to the 8 XCDs round-robin; when the
+  // column tiles split evenly, each XCD takes every eighth column tile and walks all row
+  // tiles of one before the next, so the workgroups running on an XCD share W panels in
+  // its L2.
+  const int mt = (p.M + kBM - 1) / kBM, nt = (p.N + kBN - 1) / kBN;
+  int tm, tn;
+  {
+    const int L = blockIdx.x;
+    if ((nt & 7) == 0) {
+      const int li = L >> 3;
+      tm = li % mt;
+      tn = (L & 7) + 8 * (li / mt);
+    } else {
+      tm = L % mt;
+      tn = L / mt;
+    }
+  }
+  const int m0 = tm * kBM, n0 = tn * kBN;
+  const int64_t kb = (int64_t)p.K * 2;             // row stride in bytes (X and W)
+
+  TileCopy cx, cw;
+  cx.init(kb, p.M - m0, w, lane);
+  cw.init(kb, p.N - n0, w, lane);
+  const unsigned char* xbase = reinterpret_cast<const unsigned char*>(p.x + (int64_t)m0 * p.K);
+  const unsigned char* wbase = reinterpret_cast<const unsigned char*>(p.w + (int64_t)n0 * p.K);
+  const unsigned ring = dma::lds_addr(smem);
+
+  // operand read offsets within a tile: row (lane % 32) of a 32-row block, chunk 2 ks + lane / 32
+  constexpr int KS = kBK / 16;
+  const int lr = lane & 31, hh = lane >> 5;
+  unsigned opoff[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) opoff[ks] = (unsigned)(lr * kRowBytes + (((2 * ks + hh) ^ ffn_swz(lr)) << 4));
+  const unsigned xrow = (unsigned)(wm * 64) * kRowBytes;          // this wave's X rows in a tile
+  const unsigned wrow = kTileBytes + (unsigned)(wn * 128) * kRowBytes;   // this wave's W rows
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = f32x16{};
+
+  // ---- k loop: stage kt + kStages - 1 is copied while stage kt is multiplied
+  const int KT = p.K / kBK;
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s) {
+    if (s < KT) {
+      cx.issue(xbase + (int64_t)s * kRowBytes, ring + s * kStageBytes, w);
+      cw.issue(wbase + (int64_t)s * kRowBytes, ring + s * kStageBytes + kTileBytes, w);
+    }
+  }
+  dma::wait_vmcnt<(kStages - 2) * 2 * kCopiesPerWave>();          // stage 0 landed
+  __syncthreads();
+
+  for (int kt = 0; kt < KT; ++kt) {
+    const unsigned st = ring + (unsigned)(kt % kStages) * kStageBytes;
+    const bool more = kt + kStages - 1 < KT;
+    if (more) {
+      const unsigned nx = ring + (unsigned)((kt + kStages - 1) % kStages) * kStageBytes;
+      cx.issue(xbase + (int64_t)(kt + kStages - 1) * kRowBytes, nx, w);
+      cw.issue(wbase + (int64_t)(kt + kStages - 1) * kRowBytes, nx + kTileBytes, w);
+    }
+    // k steps of 16: the operands of step ks + 1 are read while the products of step ks
+    // run (two register sets); a scheduling fence after each step keeps that order
+    u32x4 a[2][4], b[2][2];
+    load_step(st + wrow, st + xrow, opoff[0], a[0], b[0]);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 1 < KS) load_step(st + wrow, st + xrow, opoff[ks + 1], a[(ks + 1) & 1], b[(ks + 1) & 1]);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = mfma_32x32x16(a[ks & 1][nb], b[ks & 1][mb], acc[nb][mb]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // stage kt + 1 must have landed; the copies of the stages after it may still fly
+    if (more) dma::wait_vmcnt<(kStages - 2) * 2 * kCopiesPerWave>();
+    else dma::wait_vmcnt<0>();
+    __syncthreads();
+  }
+
+// ---- epilogue: lane owns row m = m0 + 64 wm + 32 mb + lr; register 4i + j of block nb
+  // holds column n = n0 + 128 wn + 32 nb + 8 i + 4 hh + j.
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int nblk = n0 + 128 * wn + 32 * nb;
+    if (nblk >= p.N) continue;                     // N is a multiple of 32: whole blocks only
+    float bias[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x2 bb = *reinterpret_cast<const u32x2*>(p.bias + nblk + 8 * i + 4 * hh);
+      bias[4 * i + 0] = __uint_as_float(bb[0] << 16);
+      bias[4 * i + 1] = __uint_as_float(bb[0] & 0xffff0000u);
+      bias[4 * i + 2] = __uint_as_float(bb[1] << 16);
+      bias[4 * i + 3] = __uint_as_float(bb[1] & 0xffff0000u);
+    }
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int m = m0 + 64 * wm + 32 * mb + lr;
+      if (m >= p.M) continue;
+      const int64_t row = (int64_t)(m / p.group_rows) * p.group_stride + (m % p.group_rows);
+      uint16_t* crow = p.c + row * p.ldc + nblk + 4 * hh;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[j] = acc[nb][mb][4 * i + j] + bias[4 * i + j];
+          if (RELU) v[j] = fmaxf(v[j], 0.f);
+        }
+        const u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        *reinterpret_cast<u32x2*>(crow + 8 * i) = o;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+long long ffn_gemm_grid(int M, int N) { return (long long)((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN); }
+
+hipError_t launch_ffn_gemm(const FfnGemmParams& p, bool relu, hipStream_t stream) {
+  const unsigned grid = (unsigned)ffn_gemm_grid(p.M, p.N);
+  if (relu)
+    hipLaunchKernelGGL(ffn_gemm_kernel<true>, dim3(grid), dim3(kWaves * 64), 0, stream, p);
+  else
+    hipLaunchKernelGGL(ffn_gemm_kernel<false>, dim3(grid), dim3(kWaves * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace fa

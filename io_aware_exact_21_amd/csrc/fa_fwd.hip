@@ -430,7 +430,7 @@ __global__ __launch_bounds__(fwd_waves(D) * 64, 2) void fa_fwd_kernel(FwdParams 
   // ---- Q^T operand, resident in registers --------------------------------------------
   const int qrow = row_lo + g.lr;
   {
-    const uint16_t* qp = p.q + ((int64_t)(b * p.Sq + qrow) * p.Hq + h) * D + 8 * g.hh;
+    const uint16_t* qp = p.q + b * p.q_bstride + ((int64_t)qrow * p.Hq + h) * D + 8 * g.hh;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
       u32x4 z = {0u, 0u, 0u, 0u};
@@ -443,8 +443,8 @@ __global__ __launch_bounds__(fwd_waves(D) * 64, 2) void fa_fwd_kernel(FwdParams 
   wv.tmask = lim - 4 * g.hh;
 
   const int64_t kv_stride = (int64_t)p.Hkv * D;
-  const uint16_t* kb = p.k + ((int64_t)b * p.Skv * p.Hkv + hk) * D;
-  const uint16_t* vb = p.v + ((int64_t)b * p.Skv * p.Hkv + hk) * D;
+  const uint16_t* kb = p.k + b * p.kv_bstride + (int64_t)hk * D;
+  const uint16_t* vb = p.v + b * p.kv_bstride + (int64_t)hk * D;
   KvDma<D, BCT, NW, NS> dma;
   dma.init(kv_stride, w, lane);
 
@@ -511,7 +511,7 @@ __global__ __launch_bounds__(fwd_waves(D) * 64, 2) void fa_fwd_kernel(FwdParams 
   const float lt = pair_sum(wv.l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (qrow < p.Sq) {
-    const int64_t obase = ((int64_t)(b * p.Sq + qrow) * p.Hq + h) * D;
+    const int64_t obase = b * p.o_bstride + ((int64_t)qrow * p.Hq + h) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll

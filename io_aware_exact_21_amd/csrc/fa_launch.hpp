@@ -23,6 +23,10 @@ struct FwdParams {
   void* o;
   float* lse;
   int B, Hq, Hkv, Sq, Skv, d;
+  // elements between batch elements of q, of k and v, and of o (Sq*Hq*d, Skv*Hkv*d and
+  // Sq*Hq*d for contiguous tensors; the blockwise layer runs one row block of every
+  // batch element at once); lse is always contiguous [B, Hq, Sq]
+  int64_t q_bstride, kv_bstride, o_bstride;
   float c;          // |scale| * log2(e), or 1 when scale == 0 (then Q is zeroed)
   unsigned qsign;   // 0x80008000 when scale < 0 (negates Q exactly), else 0
   unsigned qmask;   // 0 when scale == 0 (every score is exactly 0), else all ones

@@ -384,9 +384,10 @@ def ffn_ref(h: np.ndarray, w1: np.ndarray, b1: np.ndarray, w2: np.ndarray, b2: n
     [IOP, Blockwise Parallel Transformers] applies the transformer's feed-forward
     network to the attention output and notes that it acts on every token on its own.
     The pages do not write the network out; the reading is the classic two-layer form
-    with a ReLU: relu(h W1 + b1) W2 + b2, W1 [d_model, d_ff], W2 [d_ff, d_model].
+    with a ReLU, each layer stored as a linear layer's [out, in] weight:
+    relu(h W1^T + b1) W2^T + b2, W1 [d_ff, d_model], W2 [d_model, d_ff].
     """
-    return np.maximum(h @ w1 + b1, 0.0) @ w2 + b2
+    return np.maximum(h @ w1.T + b1, 0.0) @ w2.T + b2
 
 
 def bpt_layer_ref(q: np.ndarray, k: np.ndarray, v: np.ndarray, w1: np.ndarray, b1: np.ndarray, w2: np.ndarray,

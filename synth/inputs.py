@@ -263,12 +263,13 @@ def _normal_2d(rows: int, cols: int, seed: int, tensor_id: int) -> np.ndarray:
 
 
 def make_ffn_weights(d_model: int, d_ff: int, seed: int):
-    """Feed-forward weights as bf16 bits: W1 [d_model, d_ff], b1 [d_ff], W2 [d_ff, d_model],
-    b2 [d_model]. W1 and W2 are N(0,1) / sqrt(fan-in) (so activations stay of order one),
-    the biases N(0,1) / 10; blocks of 1024 rows seeded SeedSequence(seed, (id, 0, n)) with
-    ids 6, 7, 8, 9; rounded to bf16 (RNE)."""
-    w1 = bf16_rne_bits(_normal_2d(d_model, d_ff, seed, TENSOR_W1) / np.sqrt(d_model))
+    """Feed-forward weights as bf16 bits, each layer as a linear layer's [out, in] weight:
+    W1 [d_ff, d_model], b1 [d_ff], W2 [d_model, d_ff], b2 [d_model]. W1 and W2 are
+    N(0,1) / sqrt(fan-in) (so activations stay of order one), the biases N(0,1) / 10;
+    blocks of 1024 rows seeded SeedSequence(seed, (id, 0, n)) with ids 6, 7, 8, 9;
+    rounded to bf16 (RNE)."""
+    w1 = bf16_rne_bits(_normal_2d(d_ff, d_model, seed, TENSOR_W1) / np.sqrt(d_model))
     b1 = bf16_rne_bits(_normal_2d(1, d_ff, seed, TENSOR_B1)[0] / 10.0)
-    w2 = bf16_rne_bits(_normal_2d(d_ff, d_model, seed, TENSOR_W2) / np.sqrt(d_ff))
+    w2 = bf16_rne_bits(_normal_2d(d_model, d_ff, seed, TENSOR_W2) / np.sqrt(d_ff))
     b2 = bf16_rne_bits(_normal_2d(1, d_model, seed, TENSOR_B2)[0] / 10.0)
     return w1, b1, w2, b2

@@ -212,9 +212,10 @@ def test_fwd_fp8_validation(lib):
 
 def test_bpt_validation(lib):
     from io_aware_exact_21_amd._lib import FA_ERR_ALIGN, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE
-    need = lib.fa_bpt_workspace_bytes(64, 4, 64, 1024)
-    assert need == 64 * 256 * 2 + 64 * 1024 * 2 + (32 << 20)
-    assert lib.fa_bpt_workspace_bytes(0, 4, 64, 1024) == 0
+    need = lib.fa_bpt_workspace_bytes(2, 100, 64, 4, 64, 1024)
+    assert need == 2 * 64 * 256 * 2 + 2 * 64 * 1024 * 2            # block output + hidden, two batch elements
+    assert lib.fa_bpt_workspace_bytes(2, 100, 0, 4, 64, 1024) == 0
+    assert lib.fa_bpt_workspace_bytes(2, 50, 64, 4, 64, 1024) == 2 * 50 * 256 * 2 + 2 * 50 * 1024 * 2
 
     def f(q=A, w1=A, y=A, ws=A, wsb=None, Hq=4, Hkv=2, S=100, d=64, d_ff=1024, causal=1, rows=64):
         return lib.fa_bpt_layer(q, A, A, w1, A, A, A, y, 2, Hq, Hkv, S, d, d_ff, causal, 0.1, rows, ws,
@@ -224,6 +225,7 @@ def test_bpt_validation(lib):
     assert f(y=None) == FA_ERR_NULL
     assert f(Hq=3) == FA_ERR_SHAPE
     assert f(d_ff=0) == FA_ERR_SHAPE
+    assert f(d_ff=1000) == FA_ERR_SHAPE          # not a multiple of 64
     assert f(rows=0) == FA_ERR_SHAPE
     assert f(causal=2) == FA_ERR_SHAPE
     assert f(d=96) == FA_ERR_UNSUPPORTED

@@ -56,6 +56,6 @@ def test_fwd_fp8_rejects_wrong_output_shapes():
 
 def test_bpt_layer_rejects_wrong_output_shape():
     q, k = z(1, 8, 2, 64), z(1, 8, 1, 64)
-    w1, b1, w2, b2 = z(128, 512), z(512), z(512, 128), z(128)
+    w1, b1, w2, b2 = z(512, 128), z(512), z(128, 512), z(128)
     with pytest.raises(ValueError, match="out has shape"):
         fa.bpt_layer(q, k, k, w1, b1, w2, b2, out=z(1, 8, 64))

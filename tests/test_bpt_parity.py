@@ -6,7 +6,8 @@ only): the attention output h reaches the first GEMM rounded to bf16 (relative 2
 hidden activations m = relu(h W1 + b1) are rounded to bf16 after the ReLU (1-Lipschitz),
 and y once more. Each element of y is a sum of thousands of independently rounded terms,
 so its error is close to normal with standard deviation (2^-8 / sqrt 3) r,
-  r_n^2 = sum_j (sum_k h_k^2 W1_kj^2 + m_j^2) W2_jn^2   (root-sum-square sensitivity);
+  r_n^2 = sum_j (sum_k h_k^2 W1_jk^2 + m_j^2) W2_nj^2   (root-sum-square sensitivity;
+  W1 [d_ff, d_model] and W2 [d_model, d_ff] are linear-layer [out, in] weights);
 per element |y' - y| <= 1e-2 + half a bf16 spacing of y + 6 sigma, and per tensor the
 forward's rel-L2 bar plus 2 ||sigma|| / ||y||. (The worst-case bound, sums of absolute
 values, reaches about 2 per element at d_model 4096 and would not catch an error in a
@@ -36,8 +37,8 @@ def fa():
 
 def _sigma(h, w1, b1, w2):
     """Standard deviation of the rounding error of y, given fp64 h [n, dm] and the weights."""
-    m = np.maximum(h @ w1 + b1, 0.0)
-    r2 = ((h ** 2) @ (w1 ** 2) + m ** 2) @ (w2 ** 2)
+    m = np.maximum(h @ w1.T + b1, 0.0)
+    r2 = ((h ** 2) @ (w1 ** 2).T + m ** 2) @ (w2 ** 2).T
     return U / math.sqrt(3.0) * np.sqrt(r2)
 
 
