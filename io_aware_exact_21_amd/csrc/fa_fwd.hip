@@ -25,10 +25,11 @@ namespace {
 
 constexpr int kFwdTile = 64;      // keys per LDS tile
 constexpr int kFwdStages = 3;     // LDS ring depth (tiles)
-// Bound on the probabilities of the max-free softmax step. A lane's sum of 16
-// probabilities bounds each of them; while it stays at or below 2^64 every p and every
-// fp32 sum of p or p*v stays far inside fp32 and bf16 range (both reach 2^127), so the
-// running max only has to move when a row's scores jump by more than 64 (log2 units).
+// Bound on the probabilities of the max-free softmax step. A row's running normaliser
+// (the sum of its probabilities against the current reference m) bounds each of them;
+// while it stays at or below 2^64, every p is at most 2^64 and every fp32 sum of p * v
+// stays finite for |v| < 2^63, so the running max only has to move when a row's scores
+// jump by more than about 64 (log2 units) above it.
 constexpr float kRescaleBound = 18446744073709551616.0f;   // 2^64
 
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
@@ -155,6 +156,27 @@ struct SlotOrder {
 
 __device__ __forceinline__ unsigned bf16_pair_sum_weights() { return 0x3F803F80u; }   // (1.0, 1.0)
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Row sums of the probabilities on the matrix cores. A P operand of the P.V product
+// (32x32x16 B layout: lane l holds query l % 32 and 8 of the 16 keys of a step, the other
+// 8 in lane l ^ 32), read as the B operand of v_mfma_f32_16x16x32_bf16, places query c's
+// 16 values at k-slots 0-7 and 16-23 and query 16 + c's at 8-15 and 24-31 of column c
+// (c = l % 16). With A row 0 = ones on k-slots 0-7 and 16-23, A row 4 = ones on 8-15 and
+// 24-31 and every other row zero, D[0][c] is query c's sum and D[4][c] query 16 + c's;
+// in the D layout (lane l: column l % 16, rows 4 (l / 16) + 0..3) element 0 of lane
+// l < 32 is then the sum of query l, and element 0 of lanes 32-63 stays unchanged. The
+// sums are exact fp32 sums of the bf16 probabilities, as the packed pair sums were.
+__device__ __forceinline__ u32x4 rowsum_ones(int lane) {
+  const bool on = ((lane & 15) == 0 && ((lane >> 4) & 1) == 0) || ((lane & 15) == 4 && ((lane >> 4) & 1) == 1);
+  const unsigned w = on ? bf16_pair_sum_weights() : 0u;
+  return u32x4{w, w, w, w};
+}
+__device__ __forceinline__ f32x4 rowsum_mfma(const u32x4& ones, const u32x4& p, f32x4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ones), __builtin_bit_cast(bf16x8, p),
+                                                  acc, 0, 0, 0);
+}
+
 // Online-softmax step of one 32-row group over one 32-key unit. `s` holds this lane's
 // 16 raw scores of query row (lane % 32); they become probabilities 2^(s*c - m) packed
 // to bf16 as the two P operands of the unit. With MASK, element e (key offset
@@ -207,14 +229,20 @@ struct FwdWave {
   f32x16 o[D / 32];           // O^T accumulator
   f32x16 s0, s1;              // scores of the even / odd unit in flight
   u32x4 p0[2], p1[2];         // bf16 probabilities of the even / odd unit
-  float m, l, alpha, c;       // running max (log2 units), normaliser, pending factor, |scale|*log2 e
+  float m, alpha, c;          // running max (log2 units), pending factor, |scale|*log2 e
+  // running normaliser in element 0 (a lane's share of its row's sum: lanes l and l ^ 32
+  // together hold it); the matrix-core row sums accumulate here, elements 1-3 stay 0
+  f32x4 lacc;
+  u32x4 ones;                 // A operand of the row-sum product (rowsum_ones)
   unsigned kb_[D / 16];       // K operand read bases (ring stage 0)
   unsigned vb_[D / 32];       // V^T operand read bases (ring stage 0)
   int nu, umask, tmask;       // live units, first masked unit, mask threshold
 
   __device__ __forceinline__ void softmax_any(const f32x16& sc, u32x4 (&pp)[2], int u) {
+    float l = lacc[0];
     if (u >= umask) softmax_unit<true>(sc, m, l, alpha, pp, c, tmask - 32 * u);
     else softmax_unit<false>(sc, m, l, alpha, pp, c, 0);
+    lacc[0] = l;
   }
   // Apply the factor of the unit just softmaxed to the accumulator: after the P.V
   // product of the previous unit, before the next one. Rare: the max moves lazily.
@@ -237,10 +265,13 @@ struct FwdWave {
   // so that its dependent MFMA chain has finished long before the next slot's softmax
   // reads the scores.
   // The softmax step skips the max reduction: p = 2^(s*c - m) against the current running
-  // max, packed to bf16, with this lane's sum of the rounded p in `ls`. Every p is <=
-  // kRescaleBound whenever ls is, so when some lane's ls exceeds that bound the slot
-  // returns false and the caller redoes the unit with the full step (which may move m);
-  // the result is then the same as taking the full step directly.
+  // max, packed to bf16. The rounded p are summed into the running normaliser on the
+  // matrix cores (two 16x16x32 products with the rowsum_ones operand per unit, the first
+  // issued as soon as the unit's first 16 keys are packed). Every p is <= kRescaleBound
+  // whenever the normaliser is, so when some row's normaliser exceeds that bound the slot
+  // restores the normaliser, returns false, and the caller redoes the unit with the full
+  // step (which may move m) before its P.V product; the result is then the same as taking
+  // the full step directly.
   __device__ __forceinline__ bool fast_slot(const unsigned (&ka)[D / 16], const unsigned (&va)[D / 32],
                                             unsigned imm, const u32x4 (&pin)[2], f32x16& sout,
                                             const f32x16& sin, u32x4 (&pout)[2]) {
@@ -249,8 +280,9 @@ struct FwdWave {
     constexpr int NQK = D / 16;           // Q.K^T MFMAs
     constexpr int N = NPV + NQK;
     constexpr int E = 16 / N;             // softmax elements per step
+    constexpr int I1 = 8 / E;             // first step after the unit's first 8 elements are packed
     const float nm = -m;
-    float ls = 0.f;
+    const float lprev = lacc[0];
     u32x4 op[N];
     float pe[16];
     unsigned pk[8];
@@ -283,22 +315,27 @@ struct FwdWave {
       } else {
         s = mfma_32x32x16(op[i], q[st], s);
       }
+      if (i == I1) {
+        pout[0] = u32x4{pk[0], pk[1], pk[2], pk[3]};
+        lacc = rowsum_mfma(ones, pout[0], lacc);
+      }
 #pragma unroll
       for (int e = E * i; e < E * i + E; ++e) {
         pe[e] = fast_exp2(fmaf(sin[e], c, nm));
-        if (e & 1) {
-          pk[e >> 1] = pack_bf16x2(pe[e - 1], pe[e]);
-          ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[e >> 1]),
-                                               __builtin_bit_cast(bf16x2, bf16_pair_sum_weights()), ls, false);
-        }
+        if (e & 1) pk[e >> 1] = pack_bf16x2(pe[e - 1], pe[e]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    pout[0] = u32x4{pk[0], pk[1], pk[2], pk[3]};
     pout[1] = u32x4{pk[4], pk[5], pk[6], pk[7]};
+    lacc = rowsum_mfma(ones, pout[1], lacc);
     sout = s;
-    if (__ballot(!(ls <= kRescaleBound))) return false;
-    l += ls;
+    // An overflowing p (+inf) reaches other rows' sums as 0 * inf = NaN, and this file is
+    // compiled without NaN semantics, so the bound is tested on the magnitude bits, where
+    // inf and NaN compare above every finite value.
+    if (__ballot((__float_as_uint(lacc[0]) & 0x7fffffffu) > __float_as_uint(kRescaleBound))) {
+      lacc[0] = lprev;
+      return false;
+    }
     return true;
   }
   // Slot A of tile j (units 2j .. 2j + 3 live, unmasked, finite running max): PV(2j),
@@ -316,7 +353,9 @@ struct FwdWave {
   // rescale the accumulator. The unit's scores are formed again from its K tile, still
   // resident in LDS: the same MFMAs in the same order give bitwise the same scores.
   __device__ __forceinline__ void redo_unit(const unsigned (&ka)[D / 16], unsigned imm, u32x4 (&pp)[2]) {
+    float l = lacc[0];
     softmax_unit<false>(qk_unit<D>(ka, imm, q), m, l, alpha, pp, c, 0);
+    lacc[0] = l;
     rescale();
   }
   __device__ __forceinline__ void tile_addrs(int j, unsigned (&ka)[D / 16], unsigned (&va)[D / 32],
@@ -451,7 +490,8 @@ __global__ __launch_bounds__(fwd_waves(D) * 64, 2) void fa_fwd_kernel(FwdParams 
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) wv.o[i] = f32x16{};
   wv.m = -INFINITY;
-  wv.l = 0.f;
+  wv.lacc = f32x4{};
+  wv.ones = rowsum_ones(lane);
   wv.alpha = 1.f;
   wv.c = p.c;
 
@@ -508,7 +548,7 @@ __global__ __launch_bounds__(fwd_waves(D) * 64, 2) void fa_fwd_kernel(FwdParams 
   }
 
   // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l) -------------------------------
-  const float lt = pair_sum(wv.l);
+  const float lt = pair_sum(wv.lacc[0]);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (qrow < p.Sq) {
     const int64_t obase = b * p.o_bstride + ((int64_t)qrow * p.Hq + h) * D;
