@@ -12,13 +12,15 @@
 //     through LDS. Per 32-key unit it forms S^T = K Q^T and dP^T = V dO^T (a lane owns
 //     one query row), builds dS^T in registers and accumulates dQ^T += K^T dS^T. It also
 //     writes D.
-//   * fa_bwd_dkdv_kernel: one workgroup per (batch, KV head, 128 keys). K and V of the
-//     wave's 32 keys stay in registers; 128-row Q and dO tiles of every query head of the
-//     group stream through a two-stage LDS ring with their LSE and D rows (one barrier per
-//     four 32-query units: with one wave per SIMD every barrier drains the matrix core).
-//     Per 32-query unit it forms
-//     S = Q K^T and dP = dO V^T (a lane owns one key), and accumulates
-//     dV^T += dO^T P and dK^T += Q^T dS.
+//   * fa_bwd_dkdv_kernel (d = 64): one workgroup per (batch, KV head, 128 keys). K and V
+//     of the wave's 32 keys stay in registers; 128-row Q and dO tiles of every query head
+//     of the group stream through a two-stage LDS ring with their LSE and D rows. Per
+//     32-query unit it forms S = Q K^T and dP = dO V^T (a lane owns one key), and
+//     accumulates dV^T += dO^T P and dK^T += Q^T dS.
+//   * fa_bwd_dkdv_pair_kernel (d = 128): the same work unit, with the four products of a
+//     32-query unit split over two waves of one SIMD (S, P and dV in one; dP, dS and dK
+//     in the other, one tile later, with P passed through LDS), so that each wave's
+//     accumulators and resident operands fit two waves per SIMD.
 // Splitting dQ from dK/dV costs two extra products per tile (S and dP are formed in
 // both kernels) but keeps every output written once by one workgroup.
 //
@@ -484,6 +486,204 @@ __global__ __launch_bounds__(kBwdDkvWaves * 64) void fa_bwd_dkdv_kernel(BwdParam
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// dK, dV at two waves per SIMD: one workgroup of eight waves per (batch, KV head, 128
+// keys). Waves w and w + 4 share the 32 keys k0 + 32 (w % 4) and one SIMD. The first
+// (role 0) holds K and the dV accumulators: per 32-query unit it forms S = Q K^T, the
+// probabilities P, hands P to its partner through LDS and accumulates dV^T += dO^T P.
+// The second (role 1) holds V and the dK accumulators: one tile later it forms
+// dP = dO V^T, reads P, builds dS = P (dP - D) and accumulates dK^T += Q^T dS. Each wave
+// then keeps 64 accumulator and 32 operand registers instead of twice that, so two
+// waves share a SIMD and one's LDS reads and exponentials run under the other's matrix
+// products. Q/dO tiles of BT rows stream through a three-stage ring (a tile is read by
+// role 0 in one iteration and by role 1 in the next); P goes through two slots.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdPairWaves * 64, 2) void fa_bwd_dkdv_pair_kernel(BwdParams p) {
+  constexpr int NW = kBwdPairWaves, NS = 3, NPAIR = 4, BC = 32 * NPAIR, BT = kBwdPairTile, NU = BT / 32;
+  constexpr unsigned TB = BT * D * 2;                    // bytes per Q / dO stage
+  constexpr unsigned VB = BT * 4;                        // bytes per LSE / D stage
+  constexpr unsigned PU = 2048u;                         // P bytes per wave and unit (bf16)
+  constexpr unsigned PS = NPAIR * NU * PU;               // P bytes per slot
+  // Q stages | dO stages | P slots | LSE stages | D stages
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * NS * TB + 2 * PS + 2 * NS * VB];
+  static_assert(BC == kBwdDkvKeys, "grid assumes kBwdDkvKeys keys per workgroup");
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = w & 3, role = w >> 2;
+  const int lr = lane & 31, hh = lane >> 5;
+
+  const int heads = p.B * p.Hkv;
+  const int kt = blockIdx.x / heads, hl = blockIdx.x - kt * heads;
+  const int b = hl / p.Hkv, hk = hl - b * p.Hkv;
+  const int grp = p.Hq / p.Hkv;
+  const int k0 = kt * BC;
+  const int diag = p.Skv - p.Sq;
+
+  const int nq_all = (p.Sq + BT - 1) / BT;
+  int qt0 = 0;
+  if (CAUSAL) qt0 = min(nq_all, max(0, k0 - diag) / BT);
+  const int nqt = nq_all - qt0;
+  const int n_it = nqt * grp;
+
+  const int key = k0 + 32 * pair + lr;
+  const bool kvalid = key < p.Skv;
+  const int kw_lo = k0 + 32 * pair;
+
+  // ---- resident K (role 0) or V (role 1) rows ------------------------------------------
+  u32x4 rop[D / 16];
+  {
+    const uint16_t* src = role == 0 ? p.k : p.v;
+    const int64_t off = ((int64_t)(b * p.Skv + (kvalid ? key : 0)) * p.Hkv + hk) * D + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      u32x4 z = {0u, 0u, 0u, 0u};
+      if (kvalid) z = *reinterpret_cast<const u32x4*>(src + off + 16 * s);
+      rop[s] = z;
+    }
+  }
+  wait_vmcnt<0>();
+  const float c = p.c;
+
+  const BwdGeom<D> g = make_bgeom<D>(lane);
+  const unsigned ring = lds_addr(smem);
+  const unsigned p_ring = ring + 2 * NS * TB;
+  const unsigned lse_ring = p_ring + 2 * PS;
+  const unsigned dsum_ring = lse_ring + NS * VB;
+  const int64_t q_stride = (int64_t)p.Hq * D;
+  TileDma<D, NW, BT> dma;
+  dma.init(q_stride, w, lane);
+
+  auto issue = [&](int it) {
+    const int hq = hk * grp + it / nqt;
+    const int r0 = (qt0 + it % nqt) * BT;
+    const unsigned st = (unsigned)(it % NS);
+    const int64_t hoff = ((int64_t)b * p.Sq * p.Hq + hq) * D;
+    dma.copy(p.q + hoff, q_stride, r0, p.Sq, ring + st * TB, w, lane);
+    dma.copy(p.dout + hoff, q_stride, r0, p.Sq, ring + (NS + st) * TB, w, lane);
+    // LSE (wave 0) and D (wave 1) rows of the tile; rows past Sq re-read row Sq - 1
+    if (w < 2 && lane < BT) {
+      const int64_t soff = ((int64_t)b * p.Hq + hq) * p.Sq + r0;
+      const unsigned ro = (unsigned)min(lane, p.Sq - 1 - r0) * 4u;
+      if (w == 0) dma::copy4(p.lse + soff, ro, lse_ring + st * VB);
+      else dma::copy4(p.dsum + soff, ro, dsum_ring + st * VB);
+    }
+  };
+
+  // unit-level mask: some (query, key) pair of the unit is outside the tensor or causal range
+  auto unit_masked = [&](int qu0) {
+    bool m = qu0 + 31 >= p.Sq;
+    if (CAUSAL) m = m || qu0 + diag < kw_lo + 31;
+    return m;
+  };
+  auto elem_off = [&](int qu0, int e) {
+    const int qi = qu0 + 8 * (e >> 2) + 4 * hh + (e & 3);
+    return qi >= p.Sq || (CAUSAL && key > qi + diag);
+  };
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
+
+  if (n_it > 0) issue(0);
+  if (role == 0) {
+    for (int it = 0; it <= n_it; ++it) {
+      wait_vmcnt<0>();                                   // tile it landed
+      __syncthreads();                                   // tile it - 2's stage and P slot it % 2 are free
+      if (it + 1 < n_it) issue(it + 1);
+      if (it < n_it) {
+        const unsigned st = (unsigned)(it % NS);
+        const unsigned qst = ring + st * TB, dst = ring + (NS + st) * TB, lst = lse_ring + st * VB;
+        const unsigned pslot = p_ring + (unsigned)(it & 1) * PS + (unsigned)(pair * NU) * PU;
+        const int r0 = (qt0 + it % nqt) * BT;
+#pragma unroll 1
+        for (int u = 0; u < NU; ++u) {
+          const int qu0 = r0 + 32 * u;
+          const RowOps<D> aq = load_rows<D>(qst + u * 32 * D * 2, g);
+          f32x16 s = {};
+#pragma unroll
+          for (int st2 = 0; st2 < D / 16; ++st2) s = mfma_32x32x16(aq.a[st2], rop[st2], s);   // S: queries x keys
+          const TrOps<D> tv0 = load_tr<D>(dst, 2 * u, g), tv1 = load_tr<D>(dst, 2 * u + 1, g);
+          f32x16 pr;
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const f32x4 l4 = *reinterpret_cast<const lds_f32x4*>(lds_ptr(lst + (unsigned)(32 * u + 8 * gq + 4 * hh) * 4u));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pr[4 * gq + i] = fast_exp2(fmaf(s[4 * gq + i], c, -l4[i] * kLog2e));
+          }
+          if (unit_masked(qu0)) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) pr[e] = elem_off(qu0, e) ? 0.f : pr[e];
+          }
+          const u32x4 p0 = p_operand(pr, 0), p1 = p_operand(pr, 1);
+          const unsigned pu = pslot + (unsigned)u * PU + (unsigned)lane * 16u;
+          *reinterpret_cast<lds_u32x4*>((lds_u8*)(uintptr_t)pu) = p0;
+          *reinterpret_cast<lds_u32x4*>((lds_u8*)(uintptr_t)(pu + 1024u)) = p1;
+          mm_tr_ops<D>(tv0, p0, acc);                    // dV^T += dO^T P
+          mm_tr_ops<D>(tv1, p1, acc);
+        }
+      }
+    }
+  } else {
+    for (int it = 0; it <= n_it; ++it) {
+      wait_vmcnt<0>();
+      __syncthreads();                                   // P of tile it - 1 is in slot (it - 1) % 2
+      if (it + 1 < n_it) issue(it + 1);
+      if (it > 0) {
+        const int jt = it - 1;
+        const unsigned st = (unsigned)(jt % NS);
+        const unsigned qst = ring + st * TB, dst = ring + (NS + st) * TB, sst = dsum_ring + st * VB;
+        const unsigned pslot = p_ring + (unsigned)(jt & 1) * PS + (unsigned)(pair * NU) * PU;
+        const int r0 = (qt0 + jt % nqt) * BT;
+#pragma unroll 1
+        for (int u = 0; u < NU; ++u) {
+          const int qu0 = r0 + 32 * u;
+          const RowOps<D> ad = load_rows<D>(dst + u * 32 * D * 2, g);
+          f32x16 dp = {};
+#pragma unroll
+          for (int st2 = 0; st2 < D / 16; ++st2) dp = mfma_32x32x16(ad.a[st2], rop[st2], dp);   // dP
+          const TrOps<D> tq0 = load_tr<D>(qst, 2 * u, g), tq1 = load_tr<D>(qst, 2 * u + 1, g);
+          const unsigned pu = pslot + (unsigned)u * PU + (unsigned)lane * 16u;
+          f32x16 pr;                                     // P as rounded for the dV product
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const u32x4 x = *reinterpret_cast<const lds_u32x4*>(lds_ptr(pu + 1024u * h2));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              pr[8 * h2 + 2 * i] = bf16_lo(x[i]);
+              pr[8 * h2 + 2 * i + 1] = bf16_hi(x[i]);
+            }
+          }
+          f32x16 ds;
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const f32x4 d4 = *reinterpret_cast<const lds_f32x4*>(lds_ptr(sst + (unsigned)(32 * u + 8 * gq + 4 * hh) * 4u));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ds[4 * gq + i] = pr[4 * gq + i] * (dp[4 * gq + i] - d4[i]);
+          }
+          if (unit_masked(qu0)) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) ds[e] = elem_off(qu0, e) ? 0.f : ds[e];
+          }
+          mm_tr_ops<D>(tq0, p_operand(ds, 0), acc);      // dK^T += Q^T dS
+          mm_tr_ops<D>(tq1, p_operand(ds, 1), acc);
+        }
+      }
+    }
+  }
+
+  // ---- epilogue: dV = acc (role 0), dK = scale * acc (role 1) ----------------------------
+  if (kvalid) {
+    const int64_t obase = ((int64_t)(b * p.Skv + key) * p.Hkv + hk) * D;
+    uint16_t* dst = (role == 0 ? p.dv : p.dk) + obase;
+    const float sc = role == 0 ? 1.f : p.scale;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) store4(dst + 32 * db + 8 * i + 4 * hh, acc[db], i, sc);
+  }
+}
+
 long long bwd_dq_grid(int B, int Hq, int Sq, int d) {
   return (long long)B * Hq * ((Sq + bwd_dq_rows(d) - 1) / bwd_dq_rows(d));
 }
@@ -497,8 +697,12 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
                      dim3(bwd_dq_waves(D) * 64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)bwd_dkdv_grid(p.B, p.Hkv, p.Skv)),
-                     dim3(kBwdDkvWaves * 64), 0, stream, p);
+  if constexpr (D == 128)
+    hipLaunchKernelGGL((fa_bwd_dkdv_pair_kernel<D, CAUSAL>), dim3((unsigned)bwd_dkdv_grid(p.B, p.Hkv, p.Skv)),
+                       dim3(kBwdPairWaves * 64), 0, stream, p);
+  else
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)bwd_dkdv_grid(p.B, p.Hkv, p.Skv)),
+                       dim3(kBwdDkvWaves * 64), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -7,10 +7,13 @@
 namespace fa {
 
 // Waves per backward workgroup: the dQ kernel gives each wave 32 query rows (two
-// waves per SIMD), the dK/dV kernel 32 keys (one wave per SIMD: its dK and dV
-// accumulators alone take 128 registers per lane).
+// waves per SIMD). At d = 64 the dK/dV kernel gives each wave 32 keys and both their
+// accumulators (four waves); at d = 128 two waves share 32 keys,
+// one holding K and dV, the other V and dK, so that two waves fit a SIMD.
 constexpr int kBwdDqWaves = 8;
 constexpr int kBwdDkvWaves = 4;
+constexpr int kBwdPairWaves = 8;
+constexpr int kBwdPairTile = 64;   // Q / dO rows per streamed tile of the d = 128 dK/dV kernel
 // At d = 64 a dQ workgroup has four waves (128 query rows) and two share a CU: the finer
 // grain shortens the causal tail of the small-head shapes.
 constexpr int bwd_dq_waves(int d) { return d == 64 ? 4 : kBwdDqWaves; }

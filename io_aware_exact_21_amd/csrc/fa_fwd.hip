@@ -418,9 +418,11 @@ __global__ __launch_bounds__(fwd_waves(D) * 64, 2) void fa_fwd_kernel(FwdParams 
   // ---- work unit ------------------------------------------------------------------
   // Workgroups are dealt to the 8 XCDs round-robin (block i runs on XCD i % 8). Each
   // XCD gets whole heads, so their K/V stay in that XCD's L2, and walks its share
-  // heaviest query tiles first across all of its heads (largest-first scheduling keeps
-  // the causal tail short). Shapes that do not split evenly use one global
-  // heaviest-first order.
+  // heaviest query tiles first (largest-first scheduling keeps the causal tail short).
+  // With at least 32 query tiles per head the XCD takes its heads four at a time, so
+  // the workgroups running together on it stream the K/V of four heads, not of all of
+  // them, and their L2 serves more of the re-reads, with the load balance unchanged.
+  // Shapes that do not split evenly use one global heaviest-first order.
   const int n_qt = (p.Sq + BR - 1) / BR;
   const int total = p.B * p.Hq * n_qt;
   int hl, rr;
@@ -429,9 +431,12 @@ __global__ __launch_bounds__(fwd_waves(D) * 64, 2) void fa_fwd_kernel(FwdParams 
     const int heads = p.B * p.Hq;
     if ((total & 7) == 0 && ((total >> 3) % n_qt) == 0) {
       const int hpx = (total >> 3) / n_qt;          // heads per XCD
+      const int G = (n_qt >= 32 && (hpx & 3) == 0) ? 4 : hpx;   // heads walked together
       const int li = L >> 3;
-      rr = li / hpx;
-      hl = (L & 7) * hpx + (li - rr * hpx);
+      const int grp = li / (G * n_qt);
+      const int r = li - grp * G * n_qt;
+      rr = r / G;
+      hl = (L & 7) * hpx + grp * G + (r - rr * G);
     } else {
       rr = L / heads;
       hl = L - rr * heads;

@@ -30,11 +30,18 @@ import time
 
 import numpy as np
 
-from .attention import attention_rows, kv_head_of, visible_keys, widen_bf16
+from .attention import attention_bwd_ref, attention_rows, kv_head_of, visible_keys, widen_bf16
 
 MAX_ABS = 1e-2
 REL_L2 = 4e-3
 ROW_BLOCK = 512
+# Gradients: unit roundoff of bf16 (8 significant bits), and how many bf16 roundings of
+# one factor of every product term each gradient's arithmetic contains. dQ: dS rounded
+# for its product. dV: P rounded for its product. dK: dS rounded for its product, and at
+# d = 128 formed from the P already rounded for the dV product (a second rounding of
+# the same factor; at d = 64 the bound is one rounding looser than needed).
+GRAD_TERM = 2.0 ** -8
+GRAD_ROUNDINGS = {"dQ": 1, "dK": 2, "dV": 1}
 
 _pool = None
 _pool_size = 0
@@ -154,6 +161,50 @@ def summarise(o: dict, lse: dict | None) -> dict:
     return res
 
 
+def grad_bound(ref: np.ndarray, a_ref: np.ndarray, roundings: int) -> np.ndarray:
+    """Per-element gradient bound: 1e-2, plus half a bf16 spacing at the exact value (the
+    output rounding), plus the worst case of ``roundings`` relative roundings of size at
+    most 2^-8 of one factor of every product term (a_ref: the oracle's worst-case
+    sensitivity to relative changes of that factor and of O inside D_i = dO_i . O_i)."""
+    return MAX_ABS + 0.5 * bf16_ulp(ref) + roundings * GRAD_TERM * a_ref
+
+
+def grad_rel_bound(nref: float, nr: float, roundings: int) -> float:
+    """Per-tensor rel-L2 bound: the stated 4e-3 plus twice the expected RMS of the
+    roundings (each independent, uniform in [-u, u], RMS u / sqrt(3); nr: the norm of the
+    oracle's root-sum-square sensitivity)."""
+    return REL_L2 + 2.0 * math.sqrt(roundings) * (GRAD_TERM / math.sqrt(3.0)) * (nr / nref if nref > 0 else 0.0)
+
+
+def grad_stats(g: np.ndarray, ref: np.ndarray, a_ref: np.ndarray, r_ref: np.ndarray, roundings: int) -> dict:
+    """Mergeable statistics of one gradient share against the oracle."""
+    g = np.asarray(g, dtype=np.float64)
+    fin = np.isfinite(g)
+    err = np.where(fin, np.abs(g - ref), np.inf)
+    bound = grad_bound(ref, a_ref, roundings)
+    return {"n": int(err.size), "nonfinite": int((~fin).sum()),
+            "sse": float(np.square(np.where(fin, g - ref, 0.0)).sum()), "ssr": float(np.square(ref).sum()),
+            "ssq_sens": float(np.square(r_ref).sum()),
+            "max_abs": float(err.max()) if err.size else 0.0,
+            "max_err_over_bound": float((err / bound).max()) if err.size else 0.0,
+            "over_bound": int((err > bound).sum()),
+            "over_1e-2": int((err > MAX_ABS).sum())}
+
+
+def grad_summary(parts: list, roundings: int) -> dict:
+    t = {k: sum(p[k] for p in parts) for k in ("n", "nonfinite", "sse", "ssr", "ssq_sens", "over_bound", "over_1e-2")}
+    nref = math.sqrt(t["ssr"])
+    rel = math.sqrt(t["sse"]) / nref if nref > 0 else math.sqrt(t["sse"])
+    return {"elements": t["n"], "nonfinite": t["nonfinite"], "max_abs": max(p["max_abs"] for p in parts),
+            "rel_l2": rel, "rel_l2_bound": grad_rel_bound(nref, math.sqrt(t["ssq_sens"]), roundings),
+            "max_err_over_bound": max(p["max_err_over_bound"] for p in parts),
+            "over_bound": t["over_bound"], "over_1e-2": t["over_1e-2"], "roundings": roundings}
+
+
+def grad_ok(s: dict) -> bool:
+    return s["nonfinite"] == 0 and s["over_bound"] == 0 and s["rel_l2"] <= s["rel_l2_bound"]
+
+
 def stated_ok(s: dict) -> bool:
     ok = s["O_nonfinite"] == 0 and s["O_max_abs"] <= MAX_ABS and s["O_rel_l2"] <= REL_L2
     if "LSE_max_abs" in s:
@@ -212,6 +263,20 @@ def _decode_task(args):
     return key, stats, dt
 
 
+def _bwd_task(args):
+    """One KV head of one batch element with every query head of its group: the oracle's
+    gradients and sensitivities, then statistics of each device gradient."""
+    key, q_bits, k_bits, v_bits, do_bits, causal, scale, dev = args
+    t0 = time.perf_counter()
+    ref = attention_bwd_ref(widen_bf16(q_bits), widen_bf16(k_bits), widen_bf16(v_bits), widen_bf16(do_bits),
+                            causal=causal, scale=scale, abs_terms=True)
+    dt = time.perf_counter() - t0
+    stats = {}
+    for i, name in enumerate(("dQ", "dK", "dV")):
+        stats[name] = grad_stats(dev[i], ref[i], ref[3 + i], ref[6 + i], GRAD_ROUNDINGS[name])
+    return key, stats, dt
+
+
 # ---------------------------------------------------------------- drivers
 def prefill_flops(Sq: int, Skv: int, d: int, causal: bool) -> float:
     """Counted FLOPs of one (batch, head) under the 4 d per visible (query, key) rule."""
@@ -257,6 +322,42 @@ def check_decode(q, k, v, outputs: dict, *, scale: float, batches=None, progress
             yield (b, np.ascontiguousarray(q[b]), np.ascontiguousarray(k[b]), np.ascontiguousarray(v[b]), Hkv, scale, outs)
 
     return _run(_decode_task, tasks(), len(batches), list(outputs), 4.0 * d * Skv * Hq, progress)
+
+
+def check_backward(q, k, v, do, grads, *, causal: bool, scale: float, progress=None) -> dict:
+    """Compare device gradients (dQ, dK, dV as float arrays in the layouts of q and k) with
+    the oracle over every (batch, KV head) group. q, do [B,Sq,Hq,d] and k, v [B,Skv,Hkv,d]
+    are bf16 bit arrays. Returns per gradient the merged summary (``grad_summary``) and
+    the oracle's timing."""
+    B, Sq, Hq, d = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    grp = Hq // Hkv
+    dq, dk, dv = grads
+
+    def tasks():
+        for b in range(B):
+            for hk in range(Hkv):
+                hs = slice(hk * grp, (hk + 1) * grp)
+                qs, ks = (slice(b, b + 1), slice(None), hs), (slice(b, b + 1), slice(None), slice(hk, hk + 1))
+                yield ((b, hk), np.ascontiguousarray(q[qs]), np.ascontiguousarray(k[ks]), np.ascontiguousarray(v[ks]),
+                       np.ascontiguousarray(do[qs]), causal, scale,
+                       (np.ascontiguousarray(dq[qs]), np.ascontiguousarray(dk[ks]), np.ascontiguousarray(dv[ks])))
+
+    pool = start_pool()
+    parts = {n: [] for n in GRAD_ROUNDINGS}
+    busy, done, n = 0.0, 0, B * Hkv
+    t0 = time.perf_counter()
+    for _, stats, dt in pool.imap_unordered(_bwd_task, tasks(), chunksize=1):
+        busy += dt
+        for name, st in stats.items():
+            parts[name].append(st)
+        done += 1
+        if progress is not None and (done == n or done % max(1, n // 8) == 0):
+            progress(f"oracle: {done}/{n} KV heads, {time.perf_counter() - t0:.1f} s")
+    res = {name: grad_summary(p, GRAD_ROUNDINGS[name]) for name, p in parts.items()}
+    res["_oracle"] = {"shares": n, "wall_s": time.perf_counter() - t0, "worker_busy_s": busy, "workers": pool_size(),
+                      "cpu_model": cpu_model()}
+    return res
 
 
 def _run(fn, tasks, ntasks: int, names: list, flops_per_task: float, progress) -> dict:

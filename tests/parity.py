@@ -11,6 +11,8 @@ final rounding adds at most half a spacing). fp32 outputs get the plain bound.
 import numpy as np
 import torch
 
+from oracle import fullcheck as fc
+
 MAX_ABS = 1e-2
 REL_L2 = 4e-3
 
@@ -66,29 +68,27 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
     return np.rint(x / sp) * sp
 
 
-GRAD_TERM = 2.0 ** -8
-
-
 def check_grad(g_gpu: np.ndarray, g_ref: np.ndarray, a_ref: np.ndarray, r_ref: np.ndarray, what: str) -> dict:
-    """Gradient check (bf16 output). The tolerance stated for O and LSE does not cover
-    gradients; this one follows from the arithmetic. Two roundings to bf16 (unit
-    roundoff u = 2^-8) enter every gradient element: one factor of each product term
-    (dS for dQ and dK, P for dV) is rounded before the fp32 MFMA accumulate, and D_i is
-    formed from the bf16 O the forward returns. a_ref and r_ref (oracle, abs_terms) are
-    the element's worst-case and root-sum-square first-order sensitivities to relative
-    changes of those factors, so the rounding error is at most u * a_ref and, for
-    independent roundings (relative error uniform in [-u, u], RMS u / sqrt(3)), has RMS
-    (u / sqrt(3)) * r_ref. fp32 arithmetic and the fp32 LSE add far less and are
-    covered by the forward's 1e-2. Per element:
-    |err| <= 1e-2 + half a bf16 spacing at the exact value + 2^-8 * a_ref.
-    Per tensor, the forward's rel-L2 bar plus twice the expected RMS of the rounding:
-    ||err||_2 <= 4e-3 ||g_ref||_2 + 2 (2^-8 / sqrt(3)) ||r_ref||_2.
+    """Gradient check (bf16 output), with the bound of oracle.fullcheck.grad_bound. The
+    tolerance stated for O and LSE does not cover gradients; this one follows from the
+    arithmetic. Besides the output rounding, bf16 roundings (unit roundoff u = 2^-8) of one
+    factor of every product term enter each gradient element: dS for dQ, P for dV, and for
+    dK both the rounding of dS and, at d = 128, that of the P it is formed from; D_i is
+    formed from the bf16 O the forward returns. a_ref and r_ref (oracle, abs_terms) are the
+    element's worst-case and root-sum-square first-order sensitivities to relative changes
+    of those factors, so k roundings give an error of at most k u a_ref and, independent
+    and uniform in [-u, u], an RMS of sqrt(k) (u / sqrt(3)) r_ref. fp32 arithmetic and the
+    fp32 LSE add far less and are covered by the forward's 1e-2. Per element:
+    |err| <= 1e-2 + half a bf16 spacing at the exact value + k 2^-8 a_ref.
+    Per tensor, the forward's rel-L2 bar plus twice the expected RMS of the roundings:
+    ||err||_2 <= 4e-3 ||g_ref||_2 + 2 sqrt(k) (2^-8 / sqrt(3)) ||r_ref||_2.
     """
+    k = fc.GRAD_ROUNDINGS[what]
     err = np.abs(g_gpu - g_ref)
-    bound = MAX_ABS + half_spacing_bf16(g_ref) + GRAD_TERM * a_ref
+    bound = fc.grad_bound(g_ref, a_ref, k)
     nref = np.linalg.norm(g_ref)
     rel = np.linalg.norm(g_gpu - g_ref) / nref if nref > 0 else np.linalg.norm(g_gpu)
-    rel_bound = REL_L2 + 2.0 * (GRAD_TERM / np.sqrt(3.0)) * (np.linalg.norm(r_ref) / nref if nref > 0 else 0.0)
+    rel_bound = fc.grad_rel_bound(nref, np.linalg.norm(r_ref), k)
     worst = np.unravel_index(np.argmax(err - bound), err.shape) if err.size else None
     info = {"max_abs": float(err.max()) if err.size else 0.0, "rel_l2": float(rel), "rel_l2_bound": float(rel_bound),
             "max_err_over_bound": float((err / bound).max()) if err.size else 0.0}

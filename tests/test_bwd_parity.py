@@ -3,9 +3,10 @@
 The GPU backward takes O and LSE from the GPU forward (its real inputs); the oracle
 computes the exact gradients of the forward's definition from Q, K, V and dO alone.
 Tolerance (tests.parity.check_grad): per element 1e-2 plus half a bf16 spacing at the exact
-value plus 2^-8 times the element's sensitivity to the two bf16 roundings on the path (one
-factor of every product term, and O inside D = dO . O); per tensor, rel-L2 4e-3 plus twice the
-expected RMS of that rounding (2^-8 / sqrt(3) times the root-sum-square sensitivity).
+value plus k 2^-8 times the element's sensitivity to the k bf16 roundings of one factor of
+every product term (and of O inside D = dO . O); per tensor, rel-L2 4e-3 plus twice the
+expected RMS of those roundings. The full-size workloads are checked element by element in
+test_full_parity.py.
 """
 import math
 
@@ -14,7 +15,7 @@ import pytest
 import torch
 
 from oracle.attention import attention_bwd_ref, widen_bf16
-from synth import WORKLOADS, make_grad_out, make_qkv, make_workload
+from synth import make_grad_out, make_qkv
 from tests.parity import check_grad, down, up
 
 pytestmark = pytest.mark.gpu
@@ -87,25 +88,3 @@ def test_deterministic(fa):
     b = _gpu_bwd(fa, q, k, v, do, True, 128 ** -0.5)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
-
-
-def test_full_size_long_prefill_heads(fa):
-    """MHA long prefill B2 H32 S8192 d128 causal (K x4 on 1% of positions), in the launch
-    configuration the benchmark times; every element of two whole heads is checked."""
-    w = WORKLOADS["mha8k"]
-    q, k, v = make_workload(w)
-    do = make_grad_out(w.B, w.Sq, w.Hq, w.d, w.seed)
-    print(f"full-size backward {w.name}", flush=True)
-    dq, dk, dv = _gpu_bwd(fa, q, k, v, do, w.causal, w.scale)
-    for b, h in ((0, 5), (1, 30)):
-        sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
-        ref = attention_bwd_ref(widen_bf16(q[sl]), widen_bf16(k[sl]), widen_bf16(v[sl]), widen_bf16(do[sl]),
-                                causal=True, scale=w.scale, abs_terms=True)
-        _check(dq[sl], dk[sl], dv[sl], ref)
-    # identities that hold for every head: sum_j dK_j = 0 (up to rounding) and sum_j dV_j = sum_i dO_i
-    sk = dk.float().sum(dim=1)
-    assert sk.abs().max().item() < 0.05 * dk.float().abs().sum(dim=1).max().item()
-    sv = dv.float().sum(dim=1)
-    want = torch.from_numpy(widen_bf16(do).sum(axis=1)).float().to(sv.device)
-    rel = ((sv - want).norm() / want.norm()).item()
-    assert rel < 4e-3, rel

@@ -84,3 +84,29 @@ def test_decode_every_element(fa, num_splits):
     lab = fc.label(res["bf16"], None)
     _report("decode", res, lab, num_splits=num_splits)
     assert lab == "pass", res["bf16"]
+
+
+@pytest.mark.parametrize("name", ["mha2k", "mha8k"])
+def test_backward_every_element(fa, name):
+    """Backward of a prefill workload in the benchmark's launch configuration: every
+    element of dQ, dK and dV against the oracle's gradients (each KV head with its query
+    heads in one share), within the bound that follows from the backward's bf16 roundings
+    (oracle.fullcheck.grad_bound, grad_rel_bound)."""
+    from synth import make_grad_out
+
+    w = WORKLOADS[name]
+    print(f"backward {name}: generating inputs", flush=True)
+    q, k, v = make_workload(w)
+    do = make_grad_out(w.B, w.Sq, w.Hq, w.d, w.seed)
+    tq, tk, tv, tdo = up(q), up(k), up(v), up(do)
+    o, lse = fa.fwd(tq, tk, tv, causal=w.causal, scale=w.scale)
+    dq, dk, dv = fa.bwd(tq, tk, tv, o, lse, tdo, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    grads = (_f32(dq), _f32(dk), _f32(dv))
+    del tq, tk, tv, tdo, o, lse, dq, dk, dv
+    res = fc.check_backward(q, k, v, do, grads, causal=w.causal, scale=w.scale,
+                            progress=lambda m: print(f"backward {name}: {m}", flush=True))
+    ok = all(fc.grad_ok(res[g]) for g in ("dQ", "dK", "dV"))
+    _report(name, res, "pass" if ok else "fail", direction="backward")
+    for g in ("dQ", "dK", "dV"):
+        assert fc.grad_ok(res[g]), (g, res[g])

@@ -86,3 +86,44 @@ def test_check_decode_pool(pool):
     o_bad = fc.bf16_rne(O); o_bad[2, 5, 100] -= 0.03
     res = fc.check_decode(q, k, v, {"bf16": (o_bad, L)}, scale=d ** -0.5)
     assert fc.label(res["bf16"], None) == "fail"
+
+
+def test_grad_bound_and_merge():
+    """The gradient bound: 1e-2 + half a bf16 spacing + k 2^-8 times the worst-case
+    sensitivity; statistics merged over shares equal those of the whole tensor."""
+    ref = np.array([1.0, -3.0, 0.02])
+    a = np.array([0.0, 100.0, 2.0])
+    np.testing.assert_allclose(fc.grad_bound(ref, a, 2), [1e-2 + 2.0 ** -8, 1e-2 + 2.0 ** -7 + 200 * 2.0 ** -8,
+                                                          1e-2 + 2.0 ** -14 + 4 * 2.0 ** -8])
+    assert fc.grad_rel_bound(2.0, 0.0, 1) == fc.REL_L2
+    assert fc.grad_rel_bound(2.0, 4.0, 1) == pytest.approx(fc.REL_L2 + 2 * 2.0 ** -8 / np.sqrt(3) * 2)
+    rng = np.random.default_rng(5)
+    g_ref = rng.standard_normal(50); a_r = np.abs(rng.standard_normal(50)); r_r = a_r / 3
+    g = g_ref + rng.standard_normal(50) * 1e-3
+    whole = fc.grad_summary([fc.grad_stats(g, g_ref, a_r, r_r, 2)], 2)
+    parts = fc.grad_summary([fc.grad_stats(g[:17], g_ref[:17], a_r[:17], r_r[:17], 2),
+                             fc.grad_stats(g[17:], g_ref[17:], a_r[17:], r_r[17:], 2)], 2)
+    for key in whole:
+        assert whole[key] == pytest.approx(parts[key], rel=1e-12), key
+    assert fc.grad_ok(whole)
+    g2 = g.copy(); g2[3] = np.nan
+    assert not fc.grad_ok(fc.grad_summary([fc.grad_stats(g2, g_ref, a_r, r_r, 2)], 2))
+
+
+def test_check_backward_pool(pool):
+    """Pool driver of the gradient check on a causal GQA case: the oracle's own gradients
+    rounded to bf16 pass; dK with one element moved by 0.05 fails, and only dK."""
+    from oracle.attention import attention_bwd_ref
+    from synth import make_grad_out
+    B, Hq, Hkv, S, d = 2, 4, 2, 70, 64
+    q, k, v = make_qkv(B, Hq, Hkv, S, S, d, seed=43)
+    do = make_grad_out(B, S, Hq, d, 43)
+    g = attention_bwd_ref(widen_bf16(q), widen_bf16(k), widen_bf16(v), widen_bf16(do), causal=True, scale=0.125)
+    grads = tuple(fc.bf16_rne(x).astype(np.float32) for x in g)
+    res = fc.check_backward(q, k, v, do, grads, causal=True, scale=0.125)
+    assert all(fc.grad_ok(res[n]) for n in ("dQ", "dK", "dV"))
+    assert res["dQ"]["elements"] == q.size and res["dK"]["elements"] == k.size and res["_oracle"]["shares"] == B * Hkv
+    bad = grads[1].copy(); bad[1, 20, 1, 5] += 0.05
+    res = fc.check_backward(q, k, v, do, (grads[0], bad, grads[2]), causal=True, scale=0.125)
+    assert fc.grad_ok(res["dQ"]) and fc.grad_ok(res["dV"]) and not fc.grad_ok(res["dK"])
+    assert res["dK"]["over_bound"] == 1
