@@ -39,10 +39,12 @@ PEAK_MFMA_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 PROFILES = os.path.join(ROOT, "profiles")
 # Sources each kernel family is built from: an HBM-traffic record is used only while
 # the sources it was measured on are unchanged.
-KERNEL_SOURCES = {"fwd": ["fa_device.hpp", "fa_launch.hpp", "fa_fwd.hip"],
+KERNEL_SOURCES = {"fwd": ["fa_device.hpp", "fa_dma.hpp", "fa_launch.hpp", "fa_fwd.hip"],
                   "decode": ["fa_device.hpp", "fa_launch.hpp", "fa_decode.hip"],
-                  "bwd": ["fa_device.hpp", "fa_bwd.hpp", "fa_bwd.hip"],
-                  "fp8": ["fa_device.hpp", "fa_dma.hpp", "fa_fp8.hpp", "fa_fwd_fp8.hip"]}
+                  "bwd": ["fa_device.hpp", "fa_dma.hpp", "fa_bwd.hpp", "fa_bwd.hip"],
+                  "fp8": ["fa_device.hpp", "fa_dma.hpp", "fa_fp8.hpp", "fa_fwd_fp8.hip"],
+                  "bpt": ["fa_device.hpp", "fa_dma.hpp", "fa_launch.hpp", "fa_fwd.hip", "fa_bpt.hpp", "fa_ffn.hip",
+                          "fa_api.hip"]}
 
 
 def fwd_flops(w) -> float:
@@ -136,7 +138,7 @@ def oracle_leg(key: str, w, q, k, v, outputs: dict) -> tuple:
 
 def probe_ceilings(dev, stream) -> dict:
     """Sustained matrix-core rate (bf16 32x32x16 products, random operands, two waves per
-    SIMD) and HBM read bandwidth (non-temporal 16-byte loads over 2 GiB) on this chip."""
+    SIMD) and HBM read bandwidth (non-temporal 16-byte loads over 4 GiB) on this chip."""
     import ctypes
     import torch
     lib = ctypes.CDLL(os.path.join(ROOT, "io_aware_exact_21_amd", "libfa_probe.so"))
@@ -165,9 +167,9 @@ def probe_ceilings(dev, stream) -> dict:
             raise RuntimeError("fa_probe_mfma_bf16 failed")
     ms = timed(mfma, 20)
     mfma_tf = blocks * 8 * iters * 8 * 32768.0 / (ms * 1e-3) / 1e12
-    nbytes = 2 << 30
+    nbytes = 4 << 30
     buf = torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device=dev)
-    rblocks = 512
+    rblocks = 1024                              # four waves per CU: the fastest of 512..16384 workgroups
 
     def read():
         if lib.fa_probe_hbm_read(buf.data_ptr(), nbytes, sink.data_ptr(), rblocks, sp) != 0:
@@ -179,7 +181,7 @@ def probe_ceilings(dev, stream) -> dict:
                           "probe": "fa_probe_mfma_bf16: 1024 workgroups x 8 waves (one workgroup per CU), 400 "
                                    "rounds of 8 v_mfma_f32_32x32x16_bf16 on random operands held in registers"},
             "hbm_read": {"value": round(gbs, 1), "unit": "GB/s", "frac_of_spec": round(gbs / PEAK_HBM_GBS, 4),
-                         "probe": "fa_probe_hbm_read: 2 GiB, 512 workgroups x 128 threads, each streaming its "
+                         "probe": "fa_probe_hbm_read: 4 GiB, 1024 workgroups x 128 threads, each streaming its "
                                   "own 4 MiB slice with non-temporal 16-byte loads, 8 in flight per thread"}}
 
 
@@ -372,7 +374,7 @@ def fp8_bench(fa, stream, wkey: str, w, steps: int, warmup: int) -> dict:
             "note": "fa_fwd_fp8 timed with HIP events around the call on the library's stream"}
 
 
-def bpt_bench(fa, stream, w, tq, tk, tv, steps: int, warmup: int, block_rows: int = 2048) -> dict:
+def bpt_bench(fa, stream, wkey: str, w, tq, tk, tv, steps: int, warmup: int, block_rows: int = 2048) -> dict:
     """fa_bpt_layer (attention + feed-forward network, blockwise) on the forward workload
     with d_model = Hq d and d_ff = 4 d_model, timed on its own; also the whole-sequence
     schedule (one block per batch element) for comparison.
@@ -425,7 +427,8 @@ def bpt_bench(fa, stream, w, tq, tk, tv, steps: int, warmup: int, block_rows: in
                                         "TFLOP/s": round(flops / (ms_full * 1e-3) / 1e12, 2),
                                         "workspace_bytes": nws_full},
             "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_BF16_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_BF16_TFLOPS, 4), "traffic": None,
+                         "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_BF16_TFLOPS, 4),
+                         "traffic": measured_traffic(f"fa_bpt_{wkey}_hbm_traffic.txt", "bpt"),
                          "kernel": "per block of rows of every batch element: fa_fwd_kernel + two ffn_gemm_kernel", "algorithmic_flops": flops},
             "note": "fa_bpt_layer timed with HIP events around the call on the library's stream"}
 
@@ -608,7 +611,7 @@ def main() -> int:
         rec["backward"] = backward_bench(fa, lib, stream, args.fwd_workload, wf, tq, tk, tv, o, lse, args.steps,
                                          args.warmup)
     if not args.no_bpt:
-        rec["blockwise_layer"] = bpt_bench(fa, stream, wf, tq, tk, tv, args.steps, args.warmup)
+        rec["blockwise_layer"] = bpt_bench(fa, stream, args.fwd_workload, wf, tq, tk, tv, args.steps, args.warmup)
     if not args.no_fp8:
         rec["fp8_forward"] = fp8_bench(fa, stream, args.fwd_workload, wf, args.steps, args.warmup)
     if not args.no_paged:

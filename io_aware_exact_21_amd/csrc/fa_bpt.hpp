@@ -11,7 +11,7 @@ namespace fa {
 // contiguous; w is a linear layer's [out, in] weight). Output row m goes to row
 // map(m) = (m / group_rows) * group_stride + m % group_rows of c, rows ldc elements
 // apart. Requirements (checked by the caller): K a multiple of 64, N a multiple of 32,
-// 255 * K * 2 < 2^32, pointers 16-byte aligned, ldc a multiple of 4.
+// 255 * K * 2 < 2^32, pointers 16-byte aligned, ldc a multiple of 8 (16-byte row stores).
 struct FfnGemmParams {
   const uint16_t* x;
   const uint16_t* w;

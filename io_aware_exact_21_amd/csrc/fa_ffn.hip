@@ -7,14 +7,18 @@
 // row-major, k contiguous), fp32 accumulation, the bias and the optional ReLU applied
 // to the fp32 sum, and one bf16 rounding (round-to-nearest-even) at the store.
 //
-// One workgroup of eight waves (two per SIMD) computes a 256 x 256 tile of C. Tiles of
+// One workgroup of four waves (one per SIMD) computes a 256 x 256 tile of C. Tiles of
 // kBK k-columns of X and W stream through an LDS ring of kStages stages by direct
-// global -> LDS copies, issued kStages - 1 stages ahead. The products are formed transposed, C^T = W X^T, on
-// v_mfma_f32_32x32x16_bf16: the W rows are the A operand and the X rows the B operand,
-// so in the accumulator a lane owns one row m of C and 4 consecutive n per register
-// group, which makes the bf16 stores 8 bytes wide. Each wave owns 64 rows m x 128
-// columns n (2 x 4 products per 16-wide k step, every LDS operand read feeding two or
-// four products).
+// global -> LDS copies, issued kStages - 1 stages ahead. The products are formed
+// transposed, C^T = W X^T, on v_mfma_f32_32x32x16_bf16: the W rows are the A operand and
+// the X rows the B operand, so in the accumulator a lane owns one row m of C and 4
+// consecutive n per register group; the epilogue stages the rounded tile through LDS and
+// stores whole 256-byte row segments (direct 8-byte stores from the accumulator layout
+// doubled the bytes written and made the first GEMM 14% slower). Each wave
+// owns 128 rows m x 128 columns n: 4 x 4 products per 16-wide k step, every LDS operand
+// read feeding four products, with the 256 accumulator registers in the AGPR file. (Eight
+// waves of 64 x 128, two per SIMD, read 1.5x the LDS bytes per product and ran the
+// blockwise layer 9-13% slower; 32-wide k stages were slower still.)
 #include "fa_bpt.hpp"
 #include "fa_device.hpp"
 #include "fa_dma.hpp"
@@ -23,16 +27,13 @@ namespace fa {
 
 namespace {
 
-#ifndef FA_FFN_BK
-#define FA_FFN_BK 64
-#endif
-#ifndef FA_FFN_STAGES
-#define FA_FFN_STAGES 2
-#endif
 constexpr int kBM = 256, kBN = 256;
-constexpr int kBK = FA_FFN_BK;                     // k columns per LDS stage
-constexpr int kStages = FA_FFN_STAGES;             // LDS ring depth
-constexpr int kWaves = 8;                          // 4 along m x 2 along n
+constexpr int kBK = 64;                            // k columns per LDS stage
+constexpr int kStages = 2;                         // LDS ring depth
+constexpr int kWaves = 4;                          // kWaves / 2 along m x 2 along n
+constexpr int kWavesM = kWaves / 2;
+constexpr int kWaveRows = kBM / kWavesM;          // rows m per wave
+constexpr int MB = kWaveRows / 32;
 constexpr int kRowBytes = kBK * 2;                 // bytes per tile row
 constexpr int kChunks = kRowBytes / 16;            // 16-byte chunks per tile row
 constexpr int kRowsPerCopy = 1024 / kRowBytes;     // tile rows per wave-level copy (1 KiB)
@@ -44,6 +45,7 @@ static_assert(kBK == 32 || kBK == 64, "tile depth");
 static_assert(kStages * kStageBytes <= 160 * 1024, "LDS ring");
 
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 
 // 16-byte chunk c of tile row r sits at chunk c ^ swz(r): sixteen consecutive rows read at
 // one logical chunk then fall on sixteen distinct 16-byte bank groups of the 256-byte bank
@@ -71,15 +73,15 @@ struct TileCopy {
   }
 };
 
-// Operands of one 16-wide k step: four 32-row W blocks (A operands) and two 32-row X
+// Operands of one 16-wide k step: four 32-row W blocks (A operands) and MB 32-row X
 // blocks (B operands) of this wave, at per-lane offset `off` within their 32-row blocks.
 __device__ __forceinline__ void load_step(unsigned wbase, unsigned xbase, unsigned off, u32x4 (&a)[4],
-                                          u32x4 (&b)[2]) {
+                                          u32x4 (&b)[MB]) {
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb)
     a[nb] = *reinterpret_cast<const lds_u32x4*>(dma::lds_ptr(wbase + off) + nb * 32 * kRowBytes);
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < MB; ++mb)
     b[mb] = *reinterpret_cast<const lds_u32x4*>(dma::lds_ptr(xbase + off) + mb * 32 * kRowBytes);
 }
 
@@ -88,7 +90,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_gemm_kernel(FfnGemmParams 
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages * kStageBytes];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = w & 3, wn = w >> 2;               // wave position: 64-row slab m, 128-column slab n
+  const int wm = w % kWavesM, wn = w / kWavesM;   // wave position: 128-row slab m, 128-column slab n
 
   // ---- tile of this workgroup: workgroups are dealt to the 8 XCDs round-robin; when the
   // column tiles split evenly, each XCD takes every eighth column tile and walks all row
@@ -123,14 +125,14 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_gemm_kernel(FfnGemmParams 
   unsigned opoff[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) opoff[ks] = (unsigned)(lr * kRowBytes + (((2 * ks + hh) ^ ffn_swz(lr)) << 4));
-  const unsigned xrow = (unsigned)(wm * 64) * kRowBytes;          // this wave's X rows in a tile
+  const unsigned xrow = (unsigned)(wm * kWaveRows) * kRowBytes;          // this wave's X rows in a tile
   const unsigned wrow = kTileBytes + (unsigned)(wn * 128) * kRowBytes;   // this wave's W rows
 
-  f32x16 acc[4][2];
+  f32x16 acc[4][MB];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = f32x16{};
+    for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = f32x16{};
 
   // ---- k loop: stage kt + kStages - 1 is copied while stage kt is multiplied
   const int KT = p.K / kBK;
@@ -154,7 +156,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_gemm_kernel(FfnGemmParams 
     }
     // k steps of 16: the operands of step ks + 1 are read while the products of step ks
     // run (two register sets); a scheduling fence after each step keeps that order
-    u32x4 a[2][4], b[2][2];
+    u32x4 a[2][4], b[2][MB];
     load_step(st + wrow, st + xrow, opoff[0], a[0], b[0]);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -162,7 +164,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_gemm_kernel(FfnGemmParams 
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = mfma_32x32x16(a[ks & 1][nb], b[ks & 1][mb], acc[nb][mb]);
+        for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = mfma_32x32x16(a[ks & 1][nb], b[ks & 1][mb], acc[nb][mb]);
       __builtin_amdgcn_sched_barrier(0);
     }
     // stage kt + 1 must have landed; the copies of the stages after it may still fly
@@ -171,27 +173,30 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_gemm_kernel(FfnGemmParams 
     __syncthreads();
   }
 
-// ---- epilogue: lane owns row m = m0 + 64 wm + 32 mb + lr; register 4i + j of block nb
-  // holds column n = n0 + 128 wn + 32 nb + 8 i + 4 hh + j.
+// ---- epilogue: bias, activation and bf16 rounding in registers, then the wave's
+  // kWaveRows x 128 tile goes through LDS (the ring is free after the last barrier) so that
+  // the global stores are whole 256-byte row segments, 16 lanes per row. In the registers
+  // lane (lr, hh) holds row 32 mb + lr and columns 32 nb + 8 i + 4 hh + j of the wave's tile;
+  // in LDS 16-byte chunk c of tile row r sits at chunk c ^ (r & 15) (conflict-free writes
+  // down a column and reads along a row).
+  static_assert(kWaves * kWaveRows * 256 <= kStages * kStageBytes, "epilogue staging fits the ring");
+  const unsigned stage = ring + (unsigned)w * (unsigned)(kWaveRows * 256);
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
     const int nblk = n0 + 128 * wn + 32 * nb;
-    if (nblk >= p.N) continue;                     // N is a multiple of 32: whole blocks only
     float bias[16];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const u32x2 bb = *reinterpret_cast<const u32x2*>(p.bias + nblk + 8 * i + 4 * hh);
+      u32x2 bb = {0u, 0u};
+      if (nblk < p.N) bb = *reinterpret_cast<const u32x2*>(p.bias + nblk + 8 * i + 4 * hh);
       bias[4 * i + 0] = __uint_as_float(bb[0] << 16);
       bias[4 * i + 1] = __uint_as_float(bb[0] & 0xffff0000u);
       bias[4 * i + 2] = __uint_as_float(bb[1] << 16);
       bias[4 * i + 3] = __uint_as_float(bb[1] & 0xffff0000u);
     }
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const int m = m0 + 64 * wm + 32 * mb + lr;
-      if (m >= p.M) continue;
-      const int64_t row = (int64_t)(m / p.group_rows) * p.group_stride + (m % p.group_rows);
-      uint16_t* crow = p.c + row * p.ldc + nblk + 4 * hh;
+    for (int mb = 0; mb < MB; ++mb) {
+      const int r = 32 * mb + lr;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float v[4];
@@ -201,8 +206,22 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_gemm_kernel(FfnGemmParams 
           if (RELU) v[j] = fmaxf(v[j], 0.f);
         }
         const u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-        *reinterpret_cast<u32x2*>(crow + 8 * i) = o;
+        const unsigned a = stage + (unsigned)(r * 256) + ((unsigned)((4 * nb + i) ^ (r & 15)) << 4) + 8u * hh;
+        *reinterpret_cast<lds_u32x2*>((dma::lds_u8*)(uintptr_t)a) = o;
       }
+    }
+  }
+  __syncthreads();
+  const int j = lane & 15;                         // 16-byte chunk: columns 8 j .. 8 j + 7
+  const int n = n0 + 128 * wn + 8 * j;
+#pragma unroll 4
+  for (int it = 0; it < kWaveRows / 4; ++it) {
+    const int r = 4 * it + (lane >> 4);
+    const u32x4 val = *reinterpret_cast<const lds_u32x4*>(dma::lds_ptr(stage + (unsigned)(r * 256) + ((unsigned)(j ^ (r & 15)) << 4)));
+    const int m = m0 + kWaveRows * wm + r;
+    if (m < p.M && n < p.N) {
+      const int64_t row = (int64_t)(m / p.group_rows) * p.group_stride + (m % p.group_rows);
+      *reinterpret_cast<u32x4*>(p.c + row * p.ldc + n) = val;
     }
   }
 }

@@ -30,7 +30,7 @@ import time
 
 import numpy as np
 
-from .attention import attention_bwd_ref, attention_rows, kv_head_of, visible_keys, widen_bf16
+from .attention import attention_bwd_ref, attention_rows, ffn_ref, kv_head_of, visible_keys, widen_bf16
 
 MAX_ABS = 1e-2
 REL_L2 = 4e-3
@@ -322,6 +322,100 @@ def check_decode(q, k, v, outputs: dict, *, scale: float, batches=None, progress
             yield (b, np.ascontiguousarray(q[b]), np.ascontiguousarray(k[b]), np.ascontiguousarray(v[b]), Hkv, scale, outs)
 
     return _run(_decode_task, tasks(), len(batches), list(outputs), 4.0 * d * Skv * Hq, progress)
+
+
+def _rows_task(args):
+    """One (batch, query head): the oracle's O for every row (returned whole)."""
+    key, q_bits, k_bits, v_bits, rows, Sq, causal, scale = args
+    t0 = time.perf_counter()
+    O, _ = _oracle_rows(q_bits, k_bits, v_bits, rows, Sq, causal, scale)
+    return key, O, time.perf_counter() - t0
+
+
+def attention_outputs(q, k, v, *, causal: bool, scale: float, progress=None) -> np.ndarray:
+    """The oracle's attention output O [B,Sq,Hq,d] (float64) of bf16 bit arrays q, k, v,
+    computed over the pool, one share per (batch, query head)."""
+    B, Sq, Hq, d = q.shape
+    Hkv = k.shape[2]
+    rows = np.arange(Sq)
+    out = np.zeros((B, Sq, Hq, d))
+
+    def tasks():
+        for b in range(B):
+            for h in range(Hq):
+                hk = kv_head_of(h, Hq, Hkv)
+                yield ((b, h), np.ascontiguousarray(q[b, :, h, :]), np.ascontiguousarray(k[b, :, hk, :]),
+                       np.ascontiguousarray(v[b, :, hk, :]), rows, Sq, causal, scale)
+
+    t0, done, n = time.perf_counter(), 0, B * Hq
+    for (b, h), O, _ in start_pool().imap_unordered(_rows_task, tasks(), chunksize=1):
+        out[b, :, h, :] = O
+        done += 1
+        if progress is not None and (done == n or done % max(1, n // 8) == 0):
+            progress(f"oracle attention: {done}/{n} heads, {time.perf_counter() - t0:.1f} s")
+    return out
+
+
+FFN_SIGMAS = 6.0
+
+
+def ffn_sigma(h: np.ndarray, w1: np.ndarray, b1: np.ndarray, w2: np.ndarray) -> np.ndarray:
+    """Standard deviation of the rounding error of the feed-forward output y, given the
+    fp64 input rows h [n, d_model] and weights (W1 [d_ff, d_model], W2 [d_model, d_ff]).
+    h reaches the first product rounded to bf16 (relative 2^-8), the hidden activations
+    m = relu(h W1^T + b1) are rounded to bf16 after the ReLU (1-Lipschitz), and y once
+    more at the output (half a spacing, bounded separately). Each element of y sums
+    thousands of independently rounded terms, so its error is close to normal with
+    standard deviation (2^-8 / sqrt 3) r, r_n^2 = sum_j (sum_k h_k^2 W1_jk^2 + m_j^2) W2_nj^2."""
+    m = np.maximum(h @ w1.T + b1, 0.0)
+    r2 = ((h ** 2) @ (w1 ** 2).T + m ** 2) @ (w2 ** 2).T
+    return GRAD_TERM / math.sqrt(3.0) * np.sqrt(r2)
+
+
+def ffn_bound(y: np.ndarray, sigma: np.ndarray) -> np.ndarray:
+    """Per-element bound of the blockwise layer's output: 1e-2 + half a bf16 spacing of y
+    + 6 sigma (the worst case, sums of absolute values, would not catch an error in a
+    single element at d_model 4096)."""
+    return MAX_ABS + 0.5 * bf16_ulp(y) + FFN_SIGMAS * sigma
+
+
+def check_ffn(h: np.ndarray, w_bits, y_dev: np.ndarray, *, row_block: int = 2048, progress=None) -> dict:
+    """Every element of a device feed-forward output y_dev [n, d_model] against
+    ffn_ref(h) of the oracle's rows h [n, d_model] (float64) and the bf16 weight bits
+    (W1, b1, W2, b2), in blocks of rows (multithreaded BLAS in this process). Returns
+    max-abs, rel-L2 and its bound (4e-3 + 2 ||sigma|| / ||y||), the worst error over the
+    per-element bound and the count of elements beyond it."""
+    W = [widen_bf16(x) for x in w_bits]
+    sse = ssr = ssig = 0.0
+    max_abs = worst = 0.0
+    over = nonfinite = 0
+    t0 = time.perf_counter()
+    for r0 in range(0, h.shape[0], row_block):
+        hb = h[r0:r0 + row_block]
+        y = ffn_ref(hb, *W)
+        sig = ffn_sigma(hb, W[0], W[1], W[2])
+        g = np.asarray(y_dev[r0:r0 + row_block], dtype=np.float64)
+        fin = np.isfinite(g)
+        err = np.where(fin, np.abs(g - y), np.inf)
+        bound = ffn_bound(y, sig)
+        nonfinite += int((~fin).sum())
+        sse += float(np.square(np.where(fin, g - y, 0.0)).sum())
+        ssr += float(np.square(y).sum())
+        ssig += float(np.square(sig).sum())
+        max_abs = max(max_abs, float(err.max()))
+        worst = max(worst, float((err / bound).max()))
+        over += int((err > bound).sum())
+        if progress is not None:
+            progress(f"oracle feed-forward: rows {r0 + len(hb)}/{h.shape[0]}, {time.perf_counter() - t0:.1f} s")
+    ny = math.sqrt(ssr)
+    return {"elements": int(y_dev.size), "nonfinite": nonfinite, "max_abs": max_abs,
+            "rel_l2": math.sqrt(sse) / ny if ny > 0 else math.sqrt(sse),
+            "rel_l2_bound": REL_L2 + 2.0 * math.sqrt(ssig) / ny if ny > 0 else REL_L2,
+            "max_err_over_bound": worst, "over_bound": over, "wall_s": time.perf_counter() - t0}
+
+
+def ffn_ok(s: dict) -> bool:
+    return s["nonfinite"] == 0 and s["over_bound"] == 0 and s["rel_l2"] <= s["rel_l2_bound"]
 
 
 def check_backward(q, k, v, do, grads, *, causal: bool, scale: float, progress=None) -> dict:

@@ -127,3 +127,24 @@ def test_check_backward_pool(pool):
     res = fc.check_backward(q, k, v, do, (grads[0], bad, grads[2]), causal=True, scale=0.125)
     assert fc.grad_ok(res["dQ"]) and fc.grad_ok(res["dV"]) and not fc.grad_ok(res["dK"])
     assert res["dK"]["over_bound"] == 1
+
+
+def test_attention_outputs_and_ffn_check(pool):
+    """attention_outputs equals attention_ref; check_ffn passes the oracle's own layer
+    output rounded to bf16 (in several row blocks) and fails one element moved by 0.1."""
+    from oracle.attention import ffn_ref
+    from synth import make_ffn_weights
+    B, Hq, Hkv, S, d = 2, 2, 1, 50, 64
+    q, k, v = make_qkv(B, Hq, Hkv, S, S, d, seed=44)
+    O = fc.attention_outputs(q, k, v, causal=True, scale=0.125)
+    np.testing.assert_array_equal(O, attention_ref(widen_bf16(q), widen_bf16(k), widen_bf16(v), causal=True,
+                                                   scale=0.125)[0])
+    dm = Hq * d
+    w = make_ffn_weights(dm, 4 * dm, seed=45)
+    h = O.reshape(B * S, dm)
+    y = ffn_ref(h, *[widen_bf16(x) for x in w])
+    res = fc.check_ffn(h, w, fc.bf16_rne(y), row_block=32)
+    assert fc.ffn_ok(res) and res["elements"] == y.size and res["max_abs"] > 0
+    bad = fc.bf16_rne(y); bad[77, 3] += 0.1
+    res = fc.check_ffn(h, w, bad, row_block=32)
+    assert not fc.ffn_ok(res) and res["over_bound"] == 1
