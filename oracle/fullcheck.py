@@ -30,7 +30,8 @@ import time
 
 import numpy as np
 
-from .attention import attention_bwd_ref, attention_rows, ffn_ref, kv_head_of, visible_keys, widen_bf16
+from .attention import (attention_bwd_ref, attention_rows, e4m3_value, ffn_ref, kv_head_of, visible_keys,
+                        widen_bf16)
 
 MAX_ABS = 1e-2
 REL_L2 = 4e-3
@@ -416,6 +417,117 @@ def check_ffn(h: np.ndarray, w_bits, y_dev: np.ndarray, *, row_block: int = 2048
 
 def ffn_ok(s: dict) -> bool:
     return s["nonfinite"] == 0 and s["over_bound"] == 0 and s["rel_l2"] <= s["rel_l2_bound"]
+
+
+FP8_P_ROUNDING = 2.0 ** -4        # relative rounding of a normal e4m3 value
+FP8_P_SUB = 2.0 ** -10            # absolute rounding below e4m3's normal range, in units of the row max
+
+
+def fp8_sensitivities(Q, K, V, rows, Sq: int, causal: bool, scale: float):
+    """Sensitivities of O to the e4m3 rounding of P for query rows ``rows`` of one head
+    (dequantised float64 Q [n, d], K, V [Skv, d]): A = sum_j P_ij |V_j|,
+    Bs = sum_j min(P_ij, 2^-10 Pmax_i) |V_j| and their root-sum-square forms R, Rs.
+    A normal e4m3 value is within 2^-4 of p (relative); below 2^-6 the error is absolute,
+    at most 2^-10 in units where the row's largest p is >= 1."""
+    sigma = float(np.float32(scale))
+    Skv = K.shape[0]
+    s = sigma * (Q @ K.T)
+    nvis = np.array([visible_keys(int(i), Sq, Skv, causal) for i in rows])
+    keep = np.arange(Skv)[None, :] < nvis[:, None]
+    s = np.where(keep, s, -np.inf)
+    P = np.zeros_like(s)
+    live = nvis > 0
+    if live.any():
+        w = np.exp(s[live] - s[live].max(axis=1, keepdims=True))
+        P[live] = w / w.sum(axis=1, keepdims=True)
+    aV = np.abs(V)
+    small = np.minimum(P, FP8_P_SUB * P.max(axis=1, keepdims=True))
+    return P @ aV, small @ aV, np.sqrt((P ** 2) @ (V ** 2)), np.sqrt((small ** 2) @ (V ** 2))
+
+
+def fp8_bound(O_ref, A, Bs):
+    """Per-element bound of the fp8 forward's O: 1e-2 + half a bf16 spacing + 2^-4 A + Bs."""
+    return MAX_ABS + 0.5 * bf16_ulp(O_ref) + FP8_P_ROUNDING * A + Bs
+
+
+def _fp8_task(args):
+    """One (batch, query head) of the fp8 forward: the oracle on the dequantised inputs,
+    the rounding sensitivities, then statistics of the device O and LSE."""
+    key, q8, k8, vt8, qsc, ksc, vsc, Sq, causal, scale, o_dev, lse_dev = args
+    t0 = time.perf_counter()
+    Skv = k8.shape[0]
+    Q = e4m3_value(q8) * float(qsc)
+    K = e4m3_value(k8) * float(ksc)
+    V = e4m3_value(vt8[:, :Skv]).T * float(vsc)
+    st = {"n": 0, "nonfinite": 0, "sse": 0.0, "ssr": 0.0, "ssR": 0.0, "ssRs": 0.0, "max_abs": 0.0,
+          "max_err_over_bound": 0.0, "over_bound": 0, "over_1e-2": 0}
+    L = np.full(Sq, -np.inf)
+    for r0 in range(0, Sq, ROW_BLOCK):
+        rows = np.arange(r0, min(Sq, r0 + ROW_BLOCK))
+        O, L[rows] = attention_rows(Q[rows], K, V, rows, Sq, causal, scale)
+        A, Bs, R, Rs = fp8_sensitivities(Q[rows], K, V, rows, Sq, causal, scale)
+        g = np.asarray(o_dev[rows], dtype=np.float64)
+        fin = np.isfinite(g)
+        err = np.where(fin, np.abs(g - O), np.inf)
+        bound = fp8_bound(O, A, Bs)
+        st["n"] += int(err.size)
+        st["nonfinite"] += int((~fin).sum())
+        st["sse"] += float(np.square(np.where(fin, g - O, 0.0)).sum())
+        st["ssr"] += float(np.square(O).sum())
+        st["ssR"] += float(np.square(R).sum())
+        st["ssRs"] += float(np.square(Rs).sum())
+        st["max_abs"] = max(st["max_abs"], float(err.max()))
+        st["max_err_over_bound"] = max(st["max_err_over_bound"], float((err / bound).max()))
+        st["over_bound"] += int((err > bound).sum())
+        st["over_1e-2"] += int((err > MAX_ABS).sum())
+    return key, (st, lse_stats(lse_dev, L)), time.perf_counter() - t0
+
+
+def check_fp8(q8, k8, vt8, q_scale, k_scale, v_scale, o, lse, *, causal: bool, scale: float, progress=None) -> dict:
+    """Every element of the fp8 forward's O (bound ``fp8_bound``; per tensor rel-L2 <=
+    4e-3 + (2 / sqrt 3)(2^-4 ||R|| + ||Rs||) / ||O||) and LSE (the stated bf16 bar: its
+    normaliser sums unrounded p) against the oracle on the dequantised inputs, over the
+    pool, one share per (batch, query head). q8 [B,Sq,Hq,d], k8 [B,Skv,Hkv,d], vt8
+    [B,Hkv,d,ldv] e4m3 codes; scales [B,H]; o [B,Sq,Hq,d], lse [B,Hq,Sq] device results."""
+    B, Sq, Hq, d = q8.shape
+    Hkv = k8.shape[2]
+
+    def tasks():
+        for b in range(B):
+            for h in range(Hq):
+                hk = kv_head_of(h, Hq, Hkv)
+                yield ((b, h), np.ascontiguousarray(q8[b, :, h]), np.ascontiguousarray(k8[b, :, hk]),
+                       np.ascontiguousarray(vt8[b, hk]), q_scale[b, h], k_scale[b, hk], v_scale[b, hk], Sq, causal,
+                       scale, np.ascontiguousarray(o[b, :, h]), np.ascontiguousarray(lse[b, h]))
+
+    parts, lparts = [], []
+    t0, done, n = time.perf_counter(), 0, B * Hq
+    for _, (st, sl), _ in start_pool().imap_unordered(_fp8_task, tasks(), chunksize=1):
+        parts.append(st)
+        lparts.append(sl)
+        done += 1
+        if progress is not None and (done == n or done % max(1, n // 8) == 0):
+            progress(f"oracle fp8: {done}/{n} heads, {time.perf_counter() - t0:.1f} s")
+    t = {k: sum(p[k] for p in parts) for k in ("n", "nonfinite", "sse", "ssr", "ssR", "ssRs", "over_bound", "over_1e-2")}
+    nO = math.sqrt(t["ssr"])
+    res = {"O": {"elements": t["n"], "nonfinite": t["nonfinite"], "max_abs": max(p["max_abs"] for p in parts),
+                 "rel_l2": math.sqrt(t["sse"]) / nO if nO > 0 else math.sqrt(t["sse"]),
+                 "rel_l2_bound": REL_L2 + 2.0 / math.sqrt(3.0) * (FP8_P_ROUNDING * math.sqrt(t["ssR"])
+                                                                  + math.sqrt(t["ssRs"])) / nO if nO > 0 else REL_L2,
+                 "max_err_over_bound": max(p["max_err_over_bound"] for p in parts), "over_bound": t["over_bound"],
+                 "over_1e-2": t["over_1e-2"]}}
+    lm = merge_stats(lparts)
+    res["LSE"] = {"max_abs": lm["max_abs"], "rel_l2": math.sqrt(lm["sse"] / lm["ssr"]) if lm["ssr"] > 0 else 0.0,
+                  "ninf_mismatch": lm["ninf_mismatch"], "nonfinite": lm["nonfinite"], "finite_entries": lm["n"]}
+    res["_oracle"] = {"shares": n, "wall_s": time.perf_counter() - t0, "workers": pool_size(), "cpu_model": cpu_model()}
+    return res
+
+
+def fp8_ok(res: dict) -> bool:
+    o, lse = res["O"], res["LSE"]
+    return (o["nonfinite"] == 0 and o["over_bound"] == 0 and o["rel_l2"] <= o["rel_l2_bound"]
+            and lse["ninf_mismatch"] == 0 and lse["nonfinite"] == 0 and lse["max_abs"] <= MAX_ABS
+            and lse["rel_l2"] <= REL_L2)
 
 
 def check_backward(q, k, v, do, grads, *, causal: bool, scale: float, progress=None) -> dict:

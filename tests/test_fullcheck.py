@@ -148,3 +148,19 @@ def test_attention_outputs_and_ffn_check(pool):
     bad = fc.bf16_rne(y); bad[77, 3] += 0.1
     res = fc.check_ffn(h, w, bad, row_block=32)
     assert not fc.ffn_ok(res) and res["over_bound"] == 1
+
+
+def test_check_fp8_pool(pool):
+    """The fp8 whole-tensor check: the oracle's own O rounded to bf16 with its LSE passes;
+    one O element moved by 0.2 (far beyond the e4m3 rounding bound) fails."""
+    from oracle.attention import attention_fp8_ref
+    from synth.fp8 import make_fp8_qkv
+    q8, k8, vt8, qs, ks, vs, ldv = make_fp8_qkv(1, 4, 2, 90, 90, 64, seed=46, k_stress_frac=0.05)
+    O, L = attention_fp8_ref(q8, k8, vt8, qs, ks, vs, causal=True, scale=0.125)
+    res = fc.check_fp8(q8, k8, vt8, qs, ks, vs, fc.bf16_rne(O), L, causal=True, scale=0.125)
+    assert fc.fp8_ok(res) and res["O"]["elements"] == O.size and res["_oracle"]["shares"] == 4
+    bad = fc.bf16_rne(O); bad[0, 50, 3, 9] += 0.2
+    res = fc.check_fp8(q8, k8, vt8, qs, ks, vs, bad, L, causal=True, scale=0.125)
+    assert not fc.fp8_ok(res) and res["O"]["over_bound"] == 1
+    lbad = L.copy(); lbad[0, 1, 7] += 0.05
+    assert not fc.fp8_ok(fc.check_fp8(q8, k8, vt8, qs, ks, vs, fc.bf16_rne(O), lbad, causal=True, scale=0.125))
