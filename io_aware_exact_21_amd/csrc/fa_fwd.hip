@@ -402,6 +402,15 @@ struct FwdWave {
 
 }  // namespace
 
+// The lane index (0..63) as a fresh value the compiler cannot reuse from earlier code:
+// recomputing lane-dependent values from it late keeps them out of the registers of the
+// tile loop.
+__device__ __forceinline__ unsigned opaque_lane() {
+  unsigned ln;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+  return ln;
+}
+
 template <int D, bool CAUSAL, bool OUT_F32>
 __global__ __launch_bounds__(fwd_waves(D) * 64, 2) void fa_fwd_kernel(FwdParams p) {
   constexpr int NW = fwd_waves(D);
@@ -482,9 +491,23 @@ __global__ __launch_bounds__(fwd_waves(D) * 64, 2) void fa_fwd_kernel(FwdParams 
       wv.q[s] = (z ^ p.qsign) & p.qmask;               // the sign of the scale is folded into Q
     }
   }
-  // unit u masks this lane's key offsets above tmask - 32u
-  const int lim = CAUSAL ? min(p.Skv - 1, qrow + diag) : p.Skv - 1;
-  wv.tmask = lim - 4 * g.hh;
+  // Unit u masks this lane's key offsets above tmask - 32u. At d = 64 the threshold is
+  // recomputed from an opaque read of the lane index wherever the guarded paths need it,
+  // so that it is not live through the hot loop: the kernel then fits 168 registers and
+  // three waves per SIMD (+6% on the 2k prefill). At d = 128 the register allocation that
+  // follows from the same change made the hot loop 7% slower, so the threshold stays live
+  // there (one register, spilled outside the hot loop).
+  auto lane_tmask = [&]() {
+    if constexpr (D == 64) {
+      const unsigned ln = opaque_lane();
+      const int qr = row_lo + (int)(ln & 31u);
+      const int lim = CAUSAL ? min(p.Skv - 1, qr + diag) : p.Skv - 1;
+      return lim - 4 * (int)(ln >> 5);
+    } else {
+      return wv.tmask;
+    }
+  };
+  wv.tmask = (CAUSAL ? min(p.Skv - 1, qrow + diag) : p.Skv - 1) - 4 * g.hh;
 
   const int64_t kv_stride = (int64_t)p.Hkv * D;
   const uint16_t* kb = p.k + b * p.kv_bstride + (int64_t)hk * D;
@@ -533,6 +556,7 @@ __global__ __launch_bounds__(fwd_waves(D) * 64, 2) void fa_fwd_kernel(FwdParams 
     }
     if (stop == 0) break;
     // A row max jumped inside tile j: redo that unit, finish the tile, resume.
+    wv.tmask = lane_tmask();
     unsigned ka[D / 16], va[D / 32], kj[D / 16];
     wv.tile_addrs(j, ka, va, kj);
     if (stop == 1) {
@@ -545,6 +569,7 @@ __global__ __launch_bounds__(fwd_waves(D) * 64, 2) void fa_fwd_kernel(FwdParams 
     __syncthreads();
     ++j;
   }
+  wv.tmask = lane_tmask();
   for (; j < ntiles; ++j) {
     if (j + 2 < ntiles) dma.issue(kb, vb, kv_stride, j + 2, p.Skv, ring, w, lane);
     wv.guarded_tile(j);
@@ -553,15 +578,21 @@ __global__ __launch_bounds__(fwd_waves(D) * 64, 2) void fa_fwd_kernel(FwdParams 
   }
 
   // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l) -------------------------------
+  // the lane's row again from an opaque read of the lane index: no lane-dependent output
+  // address stays live through the tile loop (at d = 128 that removed 20 of the 36 bytes per
+  // lane of spills outside the loop, at a small gain)
+  const unsigned lane_e = opaque_lane();
+  const int hh_e = (int)(lane_e >> 5);
+  const int qrow_e = row_lo + (int)(lane_e & 31u);
   const float lt = pair_sum(wv.lacc[0]);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  if (qrow < p.Sq) {
-    const int64_t obase = b * p.o_bstride + ((int64_t)qrow * p.Hq + h) * D;
+  if (qrow_e < p.Sq) {
+    const int64_t obase = b * p.o_bstride + ((int64_t)qrow_e * p.Hq + h) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int dim = 32 * db + 8 * i + 4 * g.hh;
+        const int dim = 32 * db + 8 * i + 4 * hh_e;
         const float o0 = wv.o[db][4 * i + 0] * inv, o1 = wv.o[db][4 * i + 1] * inv;
         const float o2 = wv.o[db][4 * i + 2] * inv, o3 = wv.o[db][4 * i + 3] * inv;
         if (OUT_F32) {
@@ -572,8 +603,8 @@ __global__ __launch_bounds__(fwd_waves(D) * 64, 2) void fa_fwd_kernel(FwdParams 
           *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.o) + obase + dim) = v2;
         }
       }
-    if (p.lse != nullptr && g.hh == 0)
-      p.lse[(int64_t)(b * p.Hq + h) * p.Sq + qrow] = lt > 0.f ? (wv.m + fast_log2(lt)) * kLn2 : -INFINITY;
+    if (p.lse != nullptr && hh_e == 0)
+      p.lse[(int64_t)(b * p.Hq + h) * p.Sq + qrow_e] = lt > 0.f ? (wv.m + fast_log2(lt)) * kLn2 : -INFINITY;
   }
 }
 
