@@ -144,7 +144,7 @@ __device__ __forceinline__ unsigned pack_fp8x4(float a, float b, float c, float 
 }  // namespace
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(fp8_waves(D) * 64, 2) void fa_fwd_fp8_kernel(Fp8Params p) {
+__global__ __launch_bounds__(fp8_waves(D) * 64, kFp8WavesPerSimd) void fa_fwd_fp8_kernel(Fp8Params p) {
   constexpr int NW = fp8_waves(D), BR = fp8_rows(D);
   using R = Ring<D>;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[R::kBytes];
