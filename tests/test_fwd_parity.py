@@ -173,6 +173,36 @@ def test_late_max_jumps(fa, causal):
     assert np.abs(o[0, seen, 0] - ref[None, :]).max() < 1e-2   # the dominant key's V row
 
 
+@pytest.mark.parametrize("jump", [400.0, 1024.0])
+def test_large_values_with_late_jumps(fa, jump):
+    """V scaled by 2^40 (exact in bf16) with a row max that jumps late: about 51 powers of two
+    (inside the max-free step's 2^64 bound on the normaliser, so probabilities up to about
+    2^51 multiply values up to 2^42) or about 130 (the unit is redone with the full step).
+    Every product and sum in the kernel then scales by exactly 2^40, so O must be exactly
+    2^40 times the unscaled result and the LSE identical; both also match the oracle."""
+    rng = np.random.default_rng(12)
+    B, S, H, d = 1, 1024, 2, 128
+    q = rng.standard_normal((B, S, H, d))
+    k = rng.standard_normal((B, S, H, d))
+    v = rng.standard_normal((B, S, H, d))
+    q[..., 0] = 1.0
+    k[0, 700, 0, 0] = jump
+    k[0, 900, 1, 0] = jump
+    qb, kb, vb = _bits(q), _bits(k), _bits(v)
+    vb40 = _bits(widen_bf16(vb) * 2.0 ** 40)
+    assert np.array_equal(widen_bf16(vb40), widen_bf16(vb) * 2.0 ** 40)
+    tq, tk = up(qb), up(kb)
+    o1, l1 = fa.fwd(tq, tk, up(vb), causal=False)
+    o2, l2 = fa.fwd(tq, tk, up(vb40), causal=False)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o2.float()).all()
+    assert torch.equal(o2.float(), o1.float() * 2.0 ** 40)
+    assert torch.equal(l1, l2)
+    o, l, O, L = _run_full(fa, qb, kb, vb40, False)
+    check_o(o / 2.0 ** 40, O / 2.0 ** 40, bf16=True)
+    check_lse(l, L)
+
+
 @pytest.mark.parametrize("scale", [-0.09, 0.0, 0.5])
 def test_other_scales(fa, scale):
     q, k, v = make_qkv(1, 4, 2, 100, 100, 128, seed=9)
