@@ -1,6 +1,6 @@
 // Fused exact attention forward for gfx950.
 //
-// One workgroup of eight waves (two per SIMD; four waves at d = 64, two workgroups per
+// One workgroup of eight waves (two per SIMD; at d = 64 four waves, three workgroups per
 // CU) owns BR = 256 (128) query rows of one (batch, query head); each wave owns 32 of
 // them, the 32 columns of its MFMA tiles.
 // The Q rows stay in registers for the whole kernel while K/V tiles of 64 keys

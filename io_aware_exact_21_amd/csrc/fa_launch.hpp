@@ -9,8 +9,9 @@ namespace fa {
 // Waves per prefill workgroup (32 query rows each, two waves per SIMD) and per
 // decode-split workgroup (each wave takes 32 keys of every KV tile).
 constexpr int kFwdWaves = 8;
-// At d = 64 a prefill workgroup has four waves (128 query rows) and two workgroups
-// share a CU: the finer grain shortens the causal tail of the small-head shapes.
+// At d = 64 a prefill workgroup has four waves (128 query rows) and three workgroups
+// share a CU (168 registers): the finer grain shortens the causal tail of the small-head
+// shapes.
 constexpr int fwd_waves(int d) { return d == 64 ? 4 : kFwdWaves; }
 constexpr int kDecWaves = 2;
 constexpr int kDecTile = 32 * kDecWaves;   // keys per decode KV tile
