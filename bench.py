@@ -39,12 +39,12 @@ PEAK_MFMA_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 PROFILES = os.path.join(ROOT, "profiles")
 # Sources each kernel family is built from: an HBM-traffic record is used only while
 # the sources it was measured on are unchanged.
-KERNEL_SOURCES = {"fwd": ["fa_device.hpp", "fa_dma.hpp", "fa_launch.hpp", "fa_fwd.hip"],
+KERNEL_SOURCES = {"fwd": ["fa_device.hpp", "fa_dma.hpp", "fa_launch.hpp", "fa_walk.hpp", "fa_fwd.hip"],
                   "decode": ["fa_device.hpp", "fa_launch.hpp", "fa_decode.hip"],
                   "bwd": ["fa_device.hpp", "fa_dma.hpp", "fa_bwd.hpp", "fa_bwd.hip"],
-                  "fp8": ["fa_device.hpp", "fa_dma.hpp", "fa_fp8.hpp", "fa_fwd_fp8.hip"],
-                  "bpt": ["fa_device.hpp", "fa_dma.hpp", "fa_launch.hpp", "fa_fwd.hip", "fa_bpt.hpp", "fa_ffn.hip",
-                          "fa_api.hip"]}
+                  "fp8": ["fa_device.hpp", "fa_dma.hpp", "fa_fp8.hpp", "fa_walk.hpp", "fa_fwd_fp8.hip"],
+                  "bpt": ["fa_device.hpp", "fa_dma.hpp", "fa_launch.hpp", "fa_walk.hpp", "fa_fwd.hip", "fa_bpt.hpp",
+                          "fa_ffn.hip", "fa_api.hip"]}
 
 
 def fwd_flops(w) -> float:

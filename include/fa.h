@@ -214,7 +214,10 @@ size_t fa_bwd_workspace_bytes(int B, int Hq, int Sq);
  *   P_ij = exp(scale * q_i.k_j - LSE_i) for visible j, D_i = dO_i . O_i,
  *   dS_ij = P_ij (dO_i . v_j - D_i),
  *   dV_j = sum_i P_ij dO_i, dK_j = scale sum_i dS_ij q_i, dQ_i = scale sum_j dS_ij k_j,
- * where a KV head sums over every query head of its group (GQA).
+ * where a KV head sums over every query head of its group (GQA). Arithmetic: bf16
+ * matrix-core products with fp32 accumulation; each product's bf16 factor (P for dV, dS
+ * for dQ and dK) is rounded to nearest even, D uses the bf16 O, and at d = 128 the dS of
+ * dK is formed from P as rounded for the dV product. Results are deterministic.
  *
  *   q, o, dout, dq : bf16 [B, Sq, Hq, d]   (o and lse: outputs of fa_fwd)
  *   k, v, dk, dv   : bf16 [B, Skv, Hkv, d]

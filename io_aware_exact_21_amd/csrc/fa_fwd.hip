@@ -4,7 +4,7 @@
 // CU) owns BR = 256 (128) query rows of one (batch, query head); each wave owns 32 of
 // them, the 32 columns of its MFMA tiles.
 // The Q rows stay in registers for the whole kernel while K/V tiles of 64 keys
-// stream through a three-stage LDS ring filled by direct global->LDS loads
+// stream through an LDS ring (five tiles at d = 128, three at d = 64) filled by direct global->LDS loads
 // ("I/O-Aware Kernels", section FlashAttention: Q blocks resident, K and V streamed
 // blockwise). Scores never leave registers; an online softmax keeps the running max
 // m, the normaliser l and the output accumulator of every row and rescales them by
@@ -18,13 +18,21 @@
 #include "fa_device.hpp"
 #include "fa_dma.hpp"
 #include "fa_launch.hpp"
+#include "fa_walk.hpp"
 
 namespace fa {
 
 namespace {
 
 constexpr int kFwdTile = 64;      // keys per LDS tile
-constexpr int kFwdStages = 3;     // LDS ring depth (tiles)
+// LDS ring depth in tiles; copies run NS - 1 tiles ahead of the tile in use. At d = 128
+// (one workgroup per CU) the ring holds five tiles, the whole 160 KB of LDS, so that the
+// last four tiles of a workgroup are resident together and its waves finish them without
+// barriers; at d = 64 three workgroups share a CU and the ring holds three tiles.
+#ifndef FA_FWD_NS128
+#define FA_FWD_NS128 5
+#endif
+constexpr int fwd_stages(int d) { return d == 128 ? FA_FWD_NS128 : 3; }
 // Bound on the probabilities of the max-free softmax step. A row's running normaliser
 // (the sum of its probabilities against the current reference m) bounds each of them;
 // while it stays at or below 2^64, every p is at most 2^64 and every fp32 sum of p * v
@@ -222,7 +230,7 @@ __device__ __forceinline__ void softmax_unit(f32x16 s, float& m, float& l, float
 template <int D, bool CAUSAL>
 struct FwdWave {
   static constexpr int BCT = kFwdTile;
-  static constexpr int NS = kFwdStages;
+  static constexpr int NS = fwd_stages(D);
   using R = Ring<D, BCT, NS>;
 
   u32x4 q[D / 16];            // Q^T operand (this wave's 32 rows)
@@ -415,7 +423,8 @@ template <int D, bool CAUSAL, bool OUT_F32>
 __global__ __launch_bounds__(fwd_waves(D) * 64, 2) void fa_fwd_kernel(FwdParams p) {
   constexpr int NW = fwd_waves(D);
   constexpr int BCT = kFwdTile;
-  constexpr int NS = kFwdStages;
+  constexpr int NS = fwd_stages(D);
+  constexpr int DIST = NS - 1;        // copies run DIST tiles ahead
   constexpr int BR = 32 * NW;
   using R = Ring<D, BCT, NS>;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[R::kBytes];
@@ -424,33 +433,10 @@ __global__ __launch_bounds__(fwd_waves(D) * 64, 2) void fa_fwd_kernel(FwdParams 
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: per-wave branches stay scalar
 
-  // ---- work unit ------------------------------------------------------------------
-  // Workgroups are dealt to the 8 XCDs round-robin (block i runs on XCD i % 8). Each
-  // XCD gets whole heads, so their K/V stay in that XCD's L2, and walks its share
-  // heaviest query tiles first (largest-first scheduling keeps the causal tail short).
-  // With at least 32 query tiles per head the XCD takes its heads four at a time, so
-  // the workgroups running together on it stream the K/V of four heads, not of all of
-  // them, and their L2 serves more of the re-reads, with the load balance unchanged.
-  // Shapes that do not split evenly use one global heaviest-first order.
+  // ---- work unit (heaviest causal query tiles first, whole heads per XCD) -------------
   const int n_qt = (p.Sq + BR - 1) / BR;
-  const int total = p.B * p.Hq * n_qt;
   int hl, rr;
-  {
-    const int L = blockIdx.x;
-    const int heads = p.B * p.Hq;
-    if ((total & 7) == 0 && ((total >> 3) % n_qt) == 0) {
-      const int hpx = (total >> 3) / n_qt;          // heads per XCD
-      const int G = (n_qt >= 32 && (hpx & 3) == 0) ? 4 : hpx;   // heads walked together
-      const int li = L >> 3;
-      const int grp = li / (G * n_qt);
-      const int r = li - grp * G * n_qt;
-      rr = r / G;
-      hl = (L & 7) * hpx + grp * G + (r - rr * G);
-    } else {
-      rr = L / heads;
-      hl = L - rr * heads;
-    }
-  }
+  prefill_work_unit(blockIdx.x, p.B * p.Hq, n_qt, hl, rr);
   const int qt = CAUSAL ? (n_qt - 1 - rr) : rr;
   const int b = hl / p.Hq, h = hl - b * p.Hq;
   const int hk = (h * p.Hkv) / p.Hq;
@@ -469,7 +455,12 @@ __global__ __launch_bounds__(fwd_waves(D) * 64, 2) void fa_fwd_kernel(FwdParams 
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) wv.vb_[db] = ring + R::kVBase + 2u * g.vbase[db];
 
-  const int row_lo = q0 + 32 * w;                      // first query row of this wave
+  // Waves w and w + 4 of an eight-wave workgroup run on one SIMD. Under the causal mask the
+  // 32-row blocks of a Q tile need 1 .. 8 units of the last 256 keys, so the SIMD pairs get
+  // blocks (0, 7), (1, 6), (2, 5), (3, 4): nine units each, which the waves work through
+  // without barriers once the last tiles are resident.
+  const int wr = (NW == 8 && w >= 4) ? 11 - w : w;
+  const int row_lo = q0 + 32 * wr;                     // first query row of this wave
   const int row_hi = min(row_lo + 31, p.Sq - 1);       // last real row of this wave
   // keys this wave needs, in 32-key units
   int kw = row_lo < p.Sq ? p.Skv : 0;
@@ -481,15 +472,15 @@ __global__ __launch_bounds__(fwd_waves(D) * 64, 2) void fa_fwd_kernel(FwdParams 
   wv.umask = umask;
 
   // ---- Q^T operand, resident in registers --------------------------------------------
+  // Rows past the end of the sequence (last Q tile only) load row Sq - 1 instead: finite
+  // scores whose output is never stored. Loading without a per-row branch lets all the
+  // loads of a lane go out together.
   const int qrow = row_lo + g.lr;
+  u32x4 qraw[D / 16];
   {
-    const uint16_t* qp = p.q + b * p.q_bstride + ((int64_t)qrow * p.Hq + h) * D + 8 * g.hh;
+    const uint16_t* qp = p.q + b * p.q_bstride + ((int64_t)min(qrow, p.Sq - 1) * p.Hq + h) * D + 8 * g.hh;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      u32x4 z = {0u, 0u, 0u, 0u};
-      if (qrow < p.Sq) z = *reinterpret_cast<const u32x4*>(qp + 16 * s);
-      wv.q[s] = (z ^ p.qsign) & p.qmask;               // the sign of the scale is folded into Q
-    }
+    for (int s = 0; s < D / 16; ++s) qraw[s] = *reinterpret_cast<const u32x4*>(qp + 16 * s);
   }
   // Unit u masks this lane's key offsets above tmask - 32u. At d = 64 the threshold is
   // recomputed from an opaque read of the lane index wherever the guarded paths need it,
@@ -523,11 +514,42 @@ __global__ __launch_bounds__(fwd_waves(D) * 64, 2) void fa_fwd_kernel(FwdParams 
   wv.alpha = 1.f;
   wv.c = p.c;
 
-  // ---- prologue: tiles 0 and 1 resident, then Q.K^T of units 0, 1 and softmax of 0 --
+  // ---- prologue: tiles 0 .. DIST - 1 issued, 0 and 1 resident, then Q.K^T of units 0, 1
+  // and softmax of 0
+  // Iteration j reads V of tile j and K of tile j + 1 and issues the copy of tile j + DIST
+  // into the stage of tile j - 1, which every wave has finished with at the barrier
+  // closing iteration j - 1. That barrier follows a wait for this wave's copies of tile
+  // j + 1 (the copies of later tiles may stay in flight). After iteration jl, which issues
+  // the last tile, every tile is resident: jl ends with a full wait and a barrier, and the
+  // iterations after it run with neither.
+  // The Q loads and the copies of tiles 0 and 1 are waited for together (iteration 0 reads
+  // K of tile 1 already); the copies of tiles 2 .. DIST - 1 go out after that wait, so the
+  // wait the compiler places before the first use of the Q registers (it does not see the
+  // copies, and waits for every outstanding load) finds nothing left to wait for.
+  constexpr int NB = 2 * KvDma<D, BCT, NW, NS>::NPW;   // copies per wave and tile
+  const int jl = ntiles - 1 - DIST;                      // last iteration that issues a copy
   if (ntiles > 0) dma.issue(kb, vb, kv_stride, 0, p.Skv, ring, w, lane);
   if (ntiles > 1) dma.issue(kb, vb, kv_stride, 1, p.Skv, ring, w, lane);
-  wait_vmcnt<0>();     // iteration 0 reads K of tile 1 already
+  wait_vmcnt<0>();
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    asm volatile("" : "+v"(qraw[s]));                   // the first use of Q stays after the wait
+    wv.q[s] = (qraw[s] ^ p.qsign) & p.qmask;            // the sign of the scale is folded into Q
+  }
+#pragma unroll
+  for (int t = 2; t < DIST; ++t)
+    if (t < ntiles) dma.issue(kb, vb, kv_stride, t, p.Skv, ring, w, lane);
+  if (jl < 0) wait_vmcnt<0>();                          // every tile issued: resident before the loop
   __syncthreads();
+  auto tile_end = [&](int jj) {
+    if (jj < jl) {
+      wait_vmcnt<(DIST - 2) * NB>();
+      __syncthreads();
+    } else if (jj == jl) {
+      wait_vmcnt<0>();
+      __syncthreads();
+    }
+  };
 
   if (wv.nu > 0) {
     wv.s0 = qk_unit<D>(wv.kb_, 0, wv.q);
@@ -546,13 +568,12 @@ __global__ __launch_bounds__(fwd_waves(D) * 64, 2) void fa_fwd_kernel(FwdParams 
     // hot loop: no guards, no max reductions, no accumulator rescale
     int stop = 0;
     for (; j < jf; ++j) {
-      if (j + 2 < ntiles) dma.issue(kb, vb, kv_stride, j + 2, p.Skv, ring, w, lane);
+      if (j <= jl) dma.issue(kb, vb, kv_stride, j + DIST, p.Skv, ring, w, lane);
       unsigned ka[D / 16], va[D / 32], kj[D / 16];
       wv.tile_addrs(j, ka, va, kj);
       if (!wv.fast_slot_a(ka, va)) { stop = 1; break; }
       if (!wv.fast_slot_b(ka, va)) { stop = 2; break; }
-      if (j + 2 < ntiles) wait_vmcnt<0>();
-      __syncthreads();
+      tile_end(j);
     }
     if (stop == 0) break;
     // A row max jumped inside tile j: redo that unit, finish the tile, resume.
@@ -565,16 +586,14 @@ __global__ __launch_bounds__(fwd_waves(D) * 64, 2) void fa_fwd_kernel(FwdParams 
     } else {
       wv.redo_unit(ka, 0, wv.p0);                             // unit 2j + 2
     }
-    if (j + 2 < ntiles) wait_vmcnt<0>();
-    __syncthreads();
+    tile_end(j);
     ++j;
   }
   wv.tmask = lane_tmask();
   for (; j < ntiles; ++j) {
-    if (j + 2 < ntiles) dma.issue(kb, vb, kv_stride, j + 2, p.Skv, ring, w, lane);
+    if (j <= jl) dma.issue(kb, vb, kv_stride, j + DIST, p.Skv, ring, w, lane);
     wv.guarded_tile(j);
-    if (j + 2 < ntiles) wait_vmcnt<0>();
-    __syncthreads();
+    tile_end(j);
   }
 
   // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l) -------------------------------

@@ -27,6 +27,7 @@
 #include "fa_device.hpp"
 #include "fa_dma.hpp"
 #include "fa_fp8.hpp"
+#include "fa_walk.hpp"
 
 #include <type_traits>
 
@@ -153,31 +154,10 @@ __global__ __launch_bounds__(fp8_waves(D) * 64, kFp8WavesPerSimd) void fa_fwd_fp
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, hh = lane >> 5;
 
-  // Workgroups go to the XCDs round-robin (block i runs on XCD i % 8). Each XCD gets whole
-  // heads and walks them heaviest causal query tiles first; with at least 32 query tiles
-  // per head it takes its heads four at a time, so the workgroups running together on it
-  // share the K/V of four heads in its L2 (+1-2% on the 8k prefills; with fewer tiles per
-  // head the grouping lengthens the causal tail, so all of the XCD's heads are walked
-  // together). Shapes that do not split evenly use one global heaviest-first order.
+  // work unit: heaviest causal query tiles first, whole heads per XCD
   const int n_qt = (p.Sq + BR - 1) / BR;
-  const int heads = p.B * p.Hq;
-  int rr, hl;
-  {
-    const int L = blockIdx.x;
-    const int total = heads * n_qt;
-    if ((total & 7) == 0 && ((total >> 3) % n_qt) == 0) {
-      const int hpx = (total >> 3) / n_qt;                      // heads per XCD
-      const int G = (n_qt >= 32 && (hpx & 3) == 0) ? 4 : hpx;   // heads walked together
-      const int li = L >> 3;
-      const int grp = li / (G * n_qt);
-      const int r = li - grp * G * n_qt;
-      rr = r / G;
-      hl = (L & 7) * hpx + grp * G + (r - rr * G);
-    } else {
-      rr = L / heads;
-      hl = L - rr * heads;
-    }
-  }
+  int hl, rr;
+  prefill_work_unit(blockIdx.x, p.B * p.Hq, n_qt, hl, rr);
   const int qt = CAUSAL ? n_qt - 1 - rr : rr;
   const int b = hl / p.Hq, h = hl - b * p.Hq;
   const int hk = (h * p.Hkv) / p.Hq;
