@@ -189,20 +189,19 @@ __global__ __launch_bounds__(fp8_waves(D) * 64, kFp8WavesPerSimd) void fa_fwd_fp
   const float vsc = p.v_scale[b * p.Hkv + hk];
 
   // ---- resident Q operand: row `row`, bytes 64 ks + 32 hh .. + 31 -------------------
+  // Rows past the end of the sequence load row Sq - 1 (finite scores, output not stored),
+  // so the loads need no per-row branch and go out together. They are waited for with the
+  // copies of the first two tiles, below.
+  u32x4 qraw[D / 32];
   i32x8 qop[D / 64];
   {
-    const uint8_t* qp = p.q + ((int64_t)(b * p.Sq + (valid ? row : 0)) * p.Hq + h) * D + 32 * hh;
+    const uint8_t* qp = p.q + ((int64_t)(b * p.Sq + min(row, p.Sq - 1)) * p.Hq + h) * D + 32 * hh;
 #pragma unroll
     for (int ks = 0; ks < D / 64; ++ks) {
-      u32x4 z0 = {0u, 0u, 0u, 0u}, z1 = z0;
-      if (valid) {
-        z0 = *reinterpret_cast<const u32x4*>(qp + 64 * ks);
-        z1 = *reinterpret_cast<const u32x4*>(qp + 64 * ks + 16);
-      }
-      qop[ks] = join((z0 ^ qsign) & qmask, (z1 ^ qsign) & qmask);
+      qraw[2 * ks] = *reinterpret_cast<const u32x4*>(qp + 64 * ks);
+      qraw[2 * ks + 1] = *reinterpret_cast<const u32x4*>(qp + 64 * ks + 16);
     }
   }
-  dma::wait_vmcnt<0>();                                  // only tile copies are in flight below
 
   // ---- per-lane LDS offsets: K rows of S^T tile 0 (tile 1 is 16 rows on, an immediate),
   // V^T rows 32 db + lr (db steps are immediates)
@@ -318,16 +317,37 @@ __global__ __launch_bounds__(fp8_waves(D) * 64, kFp8WavesPerSimd) void fa_fwd_fp
     }
   };
 
+  // The Q loads and the copies of tiles 0 and 1 complete together; after this wait only
+  // tile copies are in flight, which the per-tile waits below count. (The wait the
+  // compiler places before the first use of the Q registers does not see the copies and
+  // waits for every outstanding load: it is kept after this one.)
   if (ntiles > 0) cp.issue(kb, vb, kstride, p.ldv, p.Skv, 0, ring, w, lane);
   if (ntiles > 1) cp.issue(kb, vb, kstride, p.ldv, p.Skv, 1, ring, w, lane);
+  dma::wait_vmcnt<0>();
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) {
+    asm volatile("" : "+v"(qraw[i]));
+    qraw[i] = (qraw[i] ^ qsign) & qmask;
+  }
+#pragma unroll
+  for (int ks = 0; ks < D / 64; ++ks) qop[ks] = join(qraw[2 * ks], qraw[2 * ks + 1]);
+  // Iteration j waits for its tile and issues tile j + 2 into the stage of tile j - 1 after
+  // the barrier. Once no copies are left to issue, one full wait and barrier (at iteration
+  // max(0, ntiles - 2)) makes the last tiles resident everywhere, and the last iteration
+  // runs without either.
   auto sync = [&](int j) {
-    if (j + 1 < ntiles) dma::wait_vmcnt<Fp8Dma<D, NW>::NPW>();
-    else dma::wait_vmcnt<0>();
-    __syncthreads();                                     // tile j landed everywhere; tile j - 1 is free
-    if (j + 2 < ntiles) cp.issue(kb, vb, kstride, p.ldv, p.Skv, j + 2, ring, w, lane);
+    if (j + 2 < ntiles) {
+      dma::wait_vmcnt<Fp8Dma<D, NW>::NPW>();
+      __syncthreads();                                   // tile j landed everywhere; tile j - 1 is free
+      cp.issue(kb, vb, kstride, p.ldv, p.Skv, j + 2, ring, w, lane);
+    } else if (j == max(0, ntiles - 2)) {
+      dma::wait_vmcnt<0>();
+      __syncthreads();
+    }
   };
   // Tiles below tmask need no mask: one loop with the mask-free body, then the rest.
-  // Every wave passes one barrier per tile in either loop, so the barriers still match.
+  // Every wave calls sync for every tile in either loop, and whether it waits and passes a
+  // barrier depends only on j, so the barriers still match.
   int j = 0;
   const int split = min(tmask, min(nt_w, ntiles));
   for (; j < split; ++j) {
