@@ -233,46 +233,6 @@ void fa_bwd_dq_kernel(BwdParams p) {
   const int row = q0 + 32 * w + lr;
   const bool valid = row < p.Sq;
 
-  // ---- resident Q and dO rows; D = dO . O ---------------------------------------------
-  u32x4 qop[D / 16], dop[D / 16];
-  float dsum = 0.f;
-  {
-    const int64_t off = ((int64_t)(b * p.Sq + (valid ? row : 0)) * p.Hq + h) * D + 8 * hh;
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      u32x4 zq = {0u, 0u, 0u, 0u}, zd = zq, zo = zq;
-      if (valid) {
-        zq = *reinterpret_cast<const u32x4*>(p.q + off + 16 * s);
-        zd = *reinterpret_cast<const u32x4*>(p.dout + off + 16 * s);
-        zo = *reinterpret_cast<const u32x4*>(p.o + off + 16 * s);
-      }
-      qop[s] = zq;
-      dop[s] = zd;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dsum += bf16_lo(zd[i]) * bf16_lo(zo[i]) + bf16_hi(zd[i]) * bf16_hi(zo[i]);
-    }
-  }
-  dsum = pair_sum(dsum);
-  const int64_t srow = ((int64_t)b * p.Hq + h) * p.Sq + row;
-  float lse2 = 0.f;
-  if (valid) {
-    if (hh == 0) p.dsum[srow] = dsum;
-    lse2 = p.lse[srow] * kLog2e;
-  }
-  if (!(lse2 > -INFINITY)) lse2 = 0.f;                   // a row that sees no key: every p is masked
-  wait_vmcnt<0>();                                       // only tile copies are in flight below
-
-  // ---- this wave's key range -----------------------------------------------------------
-  const int row_lo = q0 + 32 * w;
-  const int row_hi = min(row_lo + 31, p.Sq - 1);
-  int kw = row_lo < p.Sq ? p.Skv : 0;
-  if (CAUSAL && row_lo < p.Sq) kw = max(0, min(p.Skv, row_hi + diag + 1));
-  const int nu = (kw + 31) / 32;                         // 32-key units this wave computes
-  int umask = p.Skv / 32;                                // units below need no per-element mask
-  if (CAUSAL) umask = min(umask, max(0, row_lo + diag + 1) / 32);
-  const int lim = valid ? (CAUSAL ? min(p.Skv - 1, row + diag) : p.Skv - 1) : -1;
-  const float c = p.c;
-
   const BwdGeom<D> g = make_bgeom<D>(lane);
   const unsigned ring = lds_addr(smem);
   const int64_t kv_stride = (int64_t)p.Hkv * D;
@@ -288,12 +248,54 @@ void fa_bwd_dq_kernel(BwdParams p) {
     dma.copy(vb, kv_stride, t * BT, p.Skv, ring + NS * TB + st, w, lane);
   };
 
+  // ---- resident Q and dO rows; D = dO . O ---------------------------------------------
+  // Rows past the end of the sequence load row Sq - 1 (no per-row branch, so all the loads
+  // go out together) and get lse2 = +inf, which makes every p, and so their dS, exactly 0.
+  // The row loads and the copies of tiles 0 and 1 are waited for together.
+  u32x4 qop[D / 16], dop[D / 16], oop[D / 16];
+  const int64_t srow = ((int64_t)b * p.Hq + h) * p.Sq + min(row, p.Sq - 1);
+  {
+    const int64_t off = ((int64_t)(b * p.Sq + min(row, p.Sq - 1)) * p.Hq + h) * D + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      qop[s] = *reinterpret_cast<const u32x4*>(p.q + off + 16 * s);
+      dop[s] = *reinterpret_cast<const u32x4*>(p.dout + off + 16 * s);
+      oop[s] = *reinterpret_cast<const u32x4*>(p.o + off + 16 * s);
+    }
+  }
+  float lse2 = p.lse[srow];
+  if (ntiles > 0) issue(0);
+  if (ntiles > 1) issue(1);
+  wait_vmcnt<0>();                                       // only tile copies are issued below
+  float dsum = 0.f;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    asm volatile("" : "+v"(dop[s]), "+v"(oop[s]));      // the first use stays after the wait
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      dsum += bf16_lo(dop[s][i]) * bf16_lo(oop[s][i]) + bf16_hi(dop[s][i]) * bf16_hi(oop[s][i]);
+  }
+  dsum = pair_sum(dsum);
+  asm volatile("" : "+v"(lse2));
+  lse2 = valid ? lse2 * kLog2e : INFINITY;
+  if (valid && hh == 0) p.dsum[srow] = dsum;
+  if (!(lse2 > -INFINITY)) lse2 = 0.f;                   // a row that sees no key: every p is masked
+
+  // ---- this wave's key range -----------------------------------------------------------
+  const int row_lo = q0 + 32 * w;
+  const int row_hi = min(row_lo + 31, p.Sq - 1);
+  int kw = row_lo < p.Sq ? p.Skv : 0;
+  if (CAUSAL && row_lo < p.Sq) kw = max(0, min(p.Skv, row_hi + diag + 1));
+  const int nu = (kw + 31) / 32;                         // 32-key units this wave computes
+  int umask = p.Skv / 32;                                // units below need no per-element mask
+  if (CAUSAL) umask = min(umask, max(0, row_lo + diag + 1) / 32);
+  const int lim = valid ? (CAUSAL ? min(p.Skv - 1, row + diag) : p.Skv - 1) : -1;
+  const float c = p.c;
+
   f32x16 acc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
 
-  if (ntiles > 0) issue(0);
-  if (ntiles > 1) issue(1);
   for (int j = 0; j < ntiles; ++j) {
     if (j + 1 < ntiles) wait_vmcnt<PER_TILE>();          // tile j landed; tile j + 1 may be in flight
     else wait_vmcnt<0>();
@@ -367,21 +369,17 @@ __global__ __launch_bounds__(kBwdDkvWaves * 64) void fa_bwd_dkdv_kernel(BwdParam
   const int kw_lo = k0 + 32 * w;                         // first key of this wave
 
   // ---- resident K and V rows -----------------------------------------------------------
+  // Keys past the end load key Skv - 1 (no per-key branch): finite data whose dK, dV rows
+  // are never stored. They are waited for together with the first tile copy, below.
   u32x4 kop[D / 16], vop[D / 16];
   {
-    const int64_t off = ((int64_t)(b * p.Skv + (kvalid ? key : 0)) * p.Hkv + hk) * D + 8 * hh;
+    const int64_t off = ((int64_t)(b * p.Skv + min(key, p.Skv - 1)) * p.Hkv + hk) * D + 8 * hh;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
-      u32x4 zk = {0u, 0u, 0u, 0u}, zv = zk;
-      if (kvalid) {
-        zk = *reinterpret_cast<const u32x4*>(p.k + off + 16 * s);
-        zv = *reinterpret_cast<const u32x4*>(p.v + off + 16 * s);
-      }
-      kop[s] = zk;
-      vop[s] = zv;
+      kop[s] = *reinterpret_cast<const u32x4*>(p.k + off + 16 * s);
+      vop[s] = *reinterpret_cast<const u32x4*>(p.v + off + 16 * s);
     }
   }
-  wait_vmcnt<0>();                                       // only tile copies are in flight below
   const float c = p.c;
 
   const BwdGeom<D> g = make_bgeom<D>(lane);
@@ -416,6 +414,7 @@ __global__ __launch_bounds__(kBwdDkvWaves * 64) void fa_bwd_dkdv_kernel(BwdParam
   }
 
   if (n_it > 0) issue(0);
+  wait_vmcnt<0>();                                       // K, V rows; only tile copies are issued below
   for (int it = 0; it < n_it; ++it) {
     wait_vmcnt<0>();                                     // tile it landed (the only copies in flight)
     __syncthreads();                                     // every wave's share landed; tile it - 1 is free
@@ -531,18 +530,15 @@ __global__ __launch_bounds__(kBwdPairWaves * 64, 2) void fa_bwd_dkdv_pair_kernel
   const int kw_lo = k0 + 32 * pair;
 
   // ---- resident K (role 0) or V (role 1) rows ------------------------------------------
+  // Keys past the end load key Skv - 1 (no per-key branch): finite data whose dK, dV rows
+  // are never stored. They are waited for together with the first tile copy, below.
   u32x4 rop[D / 16];
   {
     const uint16_t* src = role == 0 ? p.k : p.v;
-    const int64_t off = ((int64_t)(b * p.Skv + (kvalid ? key : 0)) * p.Hkv + hk) * D + 8 * hh;
+    const int64_t off = ((int64_t)(b * p.Skv + min(key, p.Skv - 1)) * p.Hkv + hk) * D + 8 * hh;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      u32x4 z = {0u, 0u, 0u, 0u};
-      if (kvalid) z = *reinterpret_cast<const u32x4*>(src + off + 16 * s);
-      rop[s] = z;
-    }
+    for (int s = 0; s < D / 16; ++s) rop[s] = *reinterpret_cast<const u32x4*>(src + off + 16 * s);
   }
-  wait_vmcnt<0>();
   const float c = p.c;
 
   const BwdGeom<D> g = make_bgeom<D>(lane);
