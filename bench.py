@@ -3,7 +3,7 @@
 One step = one pass of the whole hot path on resident synthetic inputs:
   fa_fwd on the long-prefill workload (B2 H32 S8192 d128, causal, K x4 on 1% of positions),
   then the split-KV decode (B64 Hq32 Hkv8 Skv16384 d128): chunk partials + log-sum-exp merge.
-W untimed warmup steps (default 50), then K timed steps (default 100) between device
+W untimed warmup steps (default 300), then K timed steps (default 200) between device
 synchronisations. Every kernel is bracketed by HIP events recorded on the stream the
 library launches on (torch's current stream, which is passed to the library), giving
 per-kernel average durations.
@@ -436,10 +436,12 @@ def bpt_bench(fa, stream, wkey: str, w, tq, tk, tv, steps: int, warmup: int, blo
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # The compute-bound kernels reach their sustained clock only after some tens of
-    # milliseconds of load: 50 warm-up steps (about 0.1 s) precede the 100 timed ones.
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=50)
+    # The compute-bound kernels settle at their sustained clock only after a few hundred
+    # milliseconds of load (forward rate per 200-step window: 1111 TFLOP/s in the first,
+    # 1128-1129 from the second on, flat over 4000 steps): 300 warm-up steps (about 0.5 s)
+    # precede the 200 timed ones.
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--fwd-workload", default="mha8k", choices=["tiny", "mha2k", "mha8k", "gqa32k"])
     # The decode workload splits the KV length into chunks and merges them by log-sum-exp,
     # so the bench runs two chunks per sequence; at this batch (B 64, Hkv 8) the library's
