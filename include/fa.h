@@ -180,8 +180,8 @@ int fa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, v
  * Chunks are cut from the T = ceil(max_blocks_per_seq * page_size / 64) tiles of
  * 64 keys of the longest possible sequence, the same boundaries for every
  * sequence: chunk c (0 <= c < n = num_splits) covers tiles
- * [floor(T c (3n - c) / 2n^2), floor(T (c + 1) (3n - c - 1) / 2n^2)), so chunk
- * sizes fall from about 1.5 T/n to 0.5 T/n and the grid, which issues every
+ * [floor(T c (2n - c) / n^2), floor(T (c + 1) (2n - c - 1) / n^2)), so chunk
+ * sizes fall linearly from about 2 T/n to T/n^2 and the grid, which issues every
  * sequence's first chunk before any second one, runs the largest pieces first.
  * A sequence's chunks past its own length are empty. The merge is fa_decode's. num_splits <= 0 selects the larger
  * of fa_decode_default_splits(B, Hkv, max_blocks_per_seq * page_size, d) and

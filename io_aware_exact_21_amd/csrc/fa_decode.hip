@@ -105,13 +105,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   if (PAGED) skv = min(max(p.seq_lens[b], 0), p.max_blocks << p.page_log2);
   int c0, c1;
   if (PAGED) {
-    // paged: chunk c covers tiles [T c (3n - c) / 2n^2, ...) of the T tiles of the longest
-    // possible sequence (n = nsplit): sizes fall from about 1.5 T/n to 0.5 T/n, so the
-    // chunk-major grid issues the largest pieces first and the smallest last
+    // paged: chunk c covers tiles [T c (2n - c) / n^2, ...) of the T tiles of the longest
+    // possible sequence (n = nsplit): sizes fall linearly from about 2 T/n to T/n^2, so the
+    // chunk-major grid issues the largest pieces first and ends on small ones
     const long long T = (p.Skv + kSplitAlign - 1) / kSplitAlign, n = p.nsplit, cc = cidx;
-    const long long d2 = 2 * n * n;
-    c0 = kSplitAlign * (int)(T * cc * (3 * n - cc) / d2);
-    c1 = min(skv, kSplitAlign * (int)(T * (cc + 1) * (3 * n - cc - 1) / d2));
+    const long long d2 = n * n;
+    c0 = kSplitAlign * (int)(T * cc * (2 * n - cc) / d2);
+    c1 = min(skv, kSplitAlign * (int)(T * (cc + 1) * (2 * n - cc - 1) / d2));
   } else {
     c0 = cidx * p.chunk;
     c1 = min(skv, c0 + p.chunk);
