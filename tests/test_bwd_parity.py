@@ -50,6 +50,8 @@ SMALL = [
     (1, 1, 1, 1, 1, 64), (1, 2, 2, 7, 7, 128), (1, 2, 2, 200, 200, 128), (2, 4, 2, 130, 257, 64),
     (1, 4, 1, 96, 64, 128), (1, 2, 2, 64, 300, 128), (1, 8, 2, 257, 257, 128), (2, 2, 1, 300, 129, 64),
     (1, 3, 3, 129, 129, 64), (1, 2, 1, 5, 70, 128),
+    # d = 128 dQ workgroups of 2, 6 and 8 key tiles (ring depth 4, the last tiles without barriers)
+    (1, 2, 2, 100, 100, 128), (1, 2, 1, 383, 383, 128), (1, 2, 2, 190, 450, 128),
 ]
 
 

@@ -37,6 +37,9 @@ SMALL = [
     (1, 1, 1, 1, 1, 64), (2, 2, 2, 7, 7, 64), (1, 4, 1, 33, 33, 128), (2, 4, 2, 130, 130, 64),
     (1, 2, 1, 257, 257, 128), (1, 8, 8, 64, 64, 128), (2, 8, 2, 200, 200, 128), (1, 2, 2, 5, 70, 64),
     (1, 2, 1, 70, 5, 128), (1, 16, 2, 129, 300, 128), (1, 1, 1, 300, 129, 64), (3, 3, 1, 97, 97, 64),
+    # d = 128 workgroups of 2, 6 and 8 key tiles: the copy distance and the barrier-free last
+    # tiles at and just past the ring depth
+    (1, 4, 2, 100, 100, 128), (1, 2, 2, 383, 383, 128), (1, 2, 1, 190, 450, 128),
 ]
 
 
