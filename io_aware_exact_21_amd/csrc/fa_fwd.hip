@@ -29,10 +29,7 @@ constexpr int kFwdTile = 64;      // keys per LDS tile
 // (one workgroup per CU) the ring holds five tiles, the whole 160 KB of LDS, so that the
 // last four tiles of a workgroup are resident together and its waves finish them without
 // barriers; at d = 64 three workgroups share a CU and the ring holds three tiles.
-#ifndef FA_FWD_NS128
-#define FA_FWD_NS128 5
-#endif
-constexpr int fwd_stages(int d) { return d == 128 ? FA_FWD_NS128 : 3; }
+constexpr int fwd_stages(int d) { return d == 128 ? 5 : 3; }
 // Bound on the probabilities of the max-free softmax step. A row's running normaliser
 // (the sum of its probabilities against the current reference m) bounds each of them;
 // while it stays at or below 2^64, every p is at most 2^64 and every fp32 sum of p * v
