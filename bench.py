@@ -44,7 +44,7 @@ KERNEL_SOURCES = {"fwd": ["fa_device.hpp", "fa_dma.hpp", "fa_launch.hpp", "fa_wa
                   "bwd": ["fa_device.hpp", "fa_dma.hpp", "fa_bwd.hpp", "fa_bwd.hip"],
                   "fp8": ["fa_device.hpp", "fa_dma.hpp", "fa_fp8.hpp", "fa_walk.hpp", "fa_fwd_fp8.hip"],
                   "bpt": ["fa_device.hpp", "fa_dma.hpp", "fa_launch.hpp", "fa_walk.hpp", "fa_fwd.hip", "fa_bpt.hpp",
-                          "fa_ffn.hip", "fa_api.hip"]}
+                          "fa_ffn.hip", "fa_api.hip", "fa_bwd.hpp", "fa_fp8.hpp"]}
 
 
 def fwd_flops(w) -> float:

@@ -67,3 +67,31 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def _local_includes(path):
+    """Quoted #include targets of a source file, followed through the headers it includes."""
+    import re
+    csrc = os.path.dirname(path)
+    seen, todo = set(), [os.path.basename(path)]
+    while todo:
+        name = todo.pop()
+        if name in seen:
+            continue
+        seen.add(name)
+        with open(os.path.join(csrc, name)) as f:
+            for m in re.finditer(r'^\s*#include\s+"([^"]+)"', f.read(), re.M):
+                if os.path.exists(os.path.join(csrc, m.group(1))):
+                    todo.append(m.group(1))
+    return seen
+
+
+@pytest.mark.parametrize("family", sorted(bench.KERNEL_SOURCES))
+def test_source_hash_families_cover_their_headers(family):
+    """Each family's hash covers every kernel-directory file its kernel sources include, so
+    a header change always invalidates the traffic figures measured on the old code."""
+    csrc = os.path.join(ROOT, "io_aware_exact_21_amd", "csrc")
+    listed = set(bench.KERNEL_SOURCES[family])
+    for src in (f for f in listed if f.endswith(".hip")):
+        missing = _local_includes(os.path.join(csrc, src)) - listed
+        assert not missing, (family, src, sorted(missing))
