@@ -194,6 +194,56 @@ struct TileDma {
   }
 };
 
+// One software-pipelined step of the dQ kernel at d = 128: the 16 products S^T, dP^T of the
+// next unit (alternating, each reading its LDS A operand two products ahead) with one
+// softmax-gradient element of the current unit per product; the element's exponent, its
+// exponential and its product with (dP - D) fall on consecutive steps.
+template <int D, bool MASK>
+__device__ __forceinline__ void dq_pipe_step(bool next, unsigned kn, unsigned vn, const BwdGeom<D>& g,
+                                             const u32x4 (&qop)[D / 16], const u32x4 (&dop)[D / 16],
+                                             const f32x16& sc, const f32x16& dc, f32x16& sn, f32x16& dn,
+                                             f32x16& ds, float c, float lse2, float dsum, int kbase, int lim) {
+  constexpr int N = 2 * (D / 16);      // products of the next unit
+  static_assert(N == 16, "one softmax element per product");
+  u32x4 op[N];
+  auto load = [&](int i) {
+    const unsigned base = (i & 1) ? vn : kn;
+    op[i] = *reinterpret_cast<const lds_u32x4*>(lds_ptr(base + g.row[i >> 1]));
+  };
+  float tx[16], pe[16];
+  if (next) {
+    load(0);
+    load(1);
+  }
+  tx[0] = fmaf(sc[0], c, -lse2);
+  __builtin_amdgcn_sched_barrier(0);
+  f32x16 a = {}, b = {};
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (next) {
+      if (i + 2 < N) load(i + 2);
+      if (i & 1) b = mfma_32x32x16(op[i], dop[i >> 1], b);
+      else a = mfma_32x32x16(op[i], qop[i >> 1], a);
+    }
+    pe[i] = fast_exp2(tx[i]);
+    if (i + 1 < 16) tx[i + 1] = fmaf(sc[i + 1], c, -lse2);
+    if (i >= 1) {
+      const int e = i - 1;
+      float pv = pe[e];
+      if (MASK && kbase + 8 * (e >> 2) + (e & 3) > lim) pv = 0.f;
+      ds[e] = pv * (dc[e] - dsum);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  {
+    float pv = pe[15];
+    if (MASK && kbase + 8 * 3 + 3 > lim) pv = 0.f;
+    ds[15] = pv * (dc[15] - dsum);
+  }
+  sn = a;
+  dn = b;
+}
+
 __device__ __forceinline__ float bf16_lo(unsigned x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned x) { return __uint_as_float(x & 0xffff0000u); }
 
@@ -313,6 +363,47 @@ void fa_bwd_dq_kernel(BwdParams p) {
   for (int t = 2; t < DIST; ++t)
     if (t < ntiles) issue(t);
   const int jw = max(0, ntiles - DIST);
+  if constexpr (D == 128) {
+    // Software-pipelined units: the products S^T, dP^T of unit U + 1 run under the softmax
+    // gradient of unit U, then dQ^T += K^T dS^T of unit U. Iteration j therefore reads tiles
+    // j and j + 1, and waits for both.
+    __syncthreads();                                     // tiles 0 and 1 resident everywhere
+    f32x16 sc = {}, dc = {};
+    if (nu > 0) {
+      sc = mm_rows<D>(ring, g, qop);
+      dc = mm_rows<D>(ring + NS * TB, g, dop);
+    }
+    for (int j = 0; j < ntiles; ++j) {
+      if (j < jw) {
+        wait_vmcnt<(DIST - 2) * PER_TILE>();             // tiles j and j + 1 landed
+        __syncthreads();                                 // every wave's share landed; tile j - 1 is free
+        issue(j + DIST);
+      } else if (j == jw) {
+        wait_vmcnt<0>();
+        __syncthreads();                                 // every remaining tile resident everywhere
+      }
+      const unsigned kst = ring + (unsigned)(j % NS) * TB;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int U = 2 * j + u;
+        if (U < nu) {
+          const bool next = U + 1 < nu;
+          const int Un = U + 1;
+          const unsigned kn = ring + (unsigned)((Un >> 1) % NS) * TB + (unsigned)(Un & 1) * 32 * D * 2;
+          const unsigned vn = kn + NS * TB;
+          f32x16 sn, dn, ds;
+          if (U >= umask)
+            dq_pipe_step<D, true>(next, kn, vn, g, qop, dop, sc, dc, sn, dn, ds, c, lse2, dsum, 32 * U + 4 * hh, lim);
+          else
+            dq_pipe_step<D, false>(next, kn, vn, g, qop, dop, sc, dc, sn, dn, ds, c, lse2, dsum, 0, 0);
+          mm_tr<D>(kst, 2 * u, g, p_operand(ds, 0), acc);
+          mm_tr<D>(kst, 2 * u + 1, g, p_operand(ds, 1), acc);
+          sc = sn;
+          dc = dn;
+        }
+      }
+    }
+  } else
   for (int j = 0; j < ntiles; ++j) {
     if (j < jw) {
       wait_vmcnt<(DIST - 1) * PER_TILE>();               // tile j landed; tiles j + 1 .. j + DIST - 1 may not have
