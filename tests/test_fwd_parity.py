@@ -40,6 +40,8 @@ SMALL = [
     # d = 128 workgroups of 2, 6 and 8 key tiles: the copy distance and the barrier-free last
     # tiles at and just past the ring depth
     (1, 4, 2, 100, 100, 128), (1, 2, 2, 383, 383, 128), (1, 2, 1, 190, 450, 128),
+    # four query heads per KV head at d = 128: one workgroup per KV group and 64-row Q tile
+    (1, 8, 2, 130, 250, 128), (2, 4, 1, 300, 300, 128), (1, 8, 2, 250, 130, 128),
 ]
 
 
