@@ -8,17 +8,26 @@
 // to the fp32 sum, and one bf16 rounding (round-to-nearest-even) at the store.
 //
 // One workgroup of four waves (one per SIMD) computes a 256 x 256 tile of C. Tiles of
-// kBK k-columns of X and W stream through an LDS ring of kStages stages by direct
-// global -> LDS copies, issued kStages - 1 stages ahead. The products are formed
-// transposed, C^T = W X^T, on v_mfma_f32_32x32x16_bf16: the W rows are the A operand and
-// the X rows the B operand, so in the accumulator a lane owns one row m of C and 4
-// consecutive n per register group; the epilogue stages the rounded tile through LDS and
-// stores whole 256-byte row segments (direct 8-byte stores from the accumulator layout
-// doubled the bytes written and made the first GEMM 14% slower). Each wave
-// owns 128 rows m x 128 columns n: 4 x 4 products per 16-wide k step, every LDS operand
-// read feeding four products, with the 256 accumulator registers in the AGPR file. (Eight
-// waves of 64 x 128, two per SIMD, read 1.5x the LDS bytes per product and ran the
-// blockwise layer 9-13% slower; 32-wide k stages were slower still.)
+// kBK k-columns of X and W stream through a two-stage LDS ring by direct global -> LDS
+// copies. The products are formed transposed, C^T = W X^T, on v_mfma_f32_32x32x16_bf16:
+// the W rows are the A operand and the X rows the B operand, so in the accumulator a lane
+// owns one row m of C and 4 consecutive n per register group; the epilogue stages the
+// rounded tile through LDS and stores whole 256-byte row segments (direct 8-byte stores
+// from the accumulator layout doubled the bytes written and made the first GEMM 14%
+// slower). Each wave owns 128 rows m x 128 columns n: 4 x 4 products per 16-wide k step,
+// every LDS operand read feeding four products, with the 256 accumulator registers in the
+// AGPR file. (Eight waves of 64 x 128, two per SIMD, read 1.5x the LDS bytes per product
+// and ran the blockwise layer 9-13% slower; 32-wide k stages were slower still.)
+//
+// The schedule keeps the matrix cores fed across stage boundaries: the operands of the
+// next k step are read, one 16-byte read between consecutive products, while the current
+// step's products run, and the stage's barrier sits before its last k step, whose operands
+// are already in registers. Past that barrier the last step's products overlap the reads
+// of the next stage's first operands and the copies of the stage after it. (With the
+// barrier at the stage end and the compiler's own placement of the reads, each step
+// waited for its operands and the matrix cores were busy 52% of the time.)
+#include <type_traits>
+
 #include "fa_bpt.hpp"
 #include "fa_device.hpp"
 #include "fa_dma.hpp"
@@ -30,6 +39,7 @@ namespace {
 constexpr int kBM = 256, kBN = 256;
 constexpr int kBK = 64;                            // k columns per LDS stage
 constexpr int kStages = 2;                         // LDS ring depth
+constexpr int kGroupRows = 8;                      // row tiles per group of the tile order
 constexpr int kWaves = 4;                          // kWaves / 2 along m x 2 along n
 constexpr int kWavesM = kWaves / 2;
 constexpr int kWaveRows = kBM / kWavesM;          // rows m per wave
@@ -41,7 +51,7 @@ constexpr int kCopiesPerWave = kBM / kRowsPerCopy / kWaves;   // per tile and wa
 constexpr unsigned kTileBytes = kBM * kRowBytes;   // X tile; the W tile is the same size
 constexpr unsigned kStageBytes = 2 * kTileBytes;
 constexpr int kSwzShift = kChunks == 8 ? 1 : 2;    // rows per 256-byte bank window: 2 or 4
-static_assert(kBK == 32 || kBK == 64, "tile depth");
+static_assert(kBK == 64, "tile depth: four 16-wide k steps per stage");
 static_assert(kStages * kStageBytes <= 160 * 1024, "LDS ring");
 
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
@@ -67,23 +77,7 @@ struct TileCopy {
       off[j] = (unsigned)(rg * row_stride_bytes) + (unsigned)(((lane % kChunks) ^ ffn_swz(r)) << 4);
     }
   }
-  __device__ __forceinline__ void issue(const void* base, unsigned lds, int w) const {
-#pragma unroll
-    for (int j = 0; j < kCopiesPerWave; ++j) dma::copy16(base, off[j], lds + (w + kWaves * j) * 1024);
-  }
 };
-
-// Operands of one 16-wide k step: four 32-row W blocks (A operands) and MB 32-row X
-// blocks (B operands) of this wave, at per-lane offset `off` within their 32-row blocks.
-__device__ __forceinline__ void load_step(unsigned wbase, unsigned xbase, unsigned off, u32x4 (&a)[4],
-                                          u32x4 (&b)[MB]) {
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
-    a[nb] = *reinterpret_cast<const lds_u32x4*>(dma::lds_ptr(wbase + off) + nb * 32 * kRowBytes);
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-    b[mb] = *reinterpret_cast<const lds_u32x4*>(dma::lds_ptr(xbase + off) + mb * 32 * kRowBytes);
-}
 
 template <bool RELU>
 __global__ __launch_bounds__(kWaves * 64, 1) void ffn_gemm_kernel(FfnGemmParams p) {
@@ -92,22 +86,19 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_gemm_kernel(FfnGemmParams 
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w % kWavesM, wn = w / kWavesM;   // wave position: 128-row slab m, 128-column slab n
 
-  // ---- tile of this workgroup: workgroups are dealt to the 8 XCDs round-robin; when the
-  // column tiles split evenly, each XCD takes every eighth column tile and walks all row
-  // tiles of one before the next, so the workgroups running on an XCD share W panels in
-  // its L2.
+  // ---- tile of this workgroup. Workgroups are dealt to the 8 XCDs round-robin; XCD x
+  // (blockIdx % 8) takes the x-th contiguous share of a grouped tile order that walks
+  // kGroupRows row tiles x every column tile, column by column, so the 32 workgroups an XCD
+  // runs at once cover a compact 8 x 4 block of tiles and share X and W panels in its L2.
   const int mt = (p.M + kBM - 1) / kBM, nt = (p.N + kBN - 1) / kBN;
   int tm, tn;
   {
-    const int L = blockIdx.x;
-    if ((nt & 7) == 0) {
-      const int li = L >> 3;
-      tm = li % mt;
-      tn = (L & 7) + 8 * (li / mt);
-    } else {
-      tm = L % mt;
-      tn = L / mt;
-    }
+    const int L = blockIdx.x, T = mt * nt, x = L & 7;
+    const int t = x * (T >> 3) + min(x, T & 7) + (L >> 3);   // XCD x owns the blockIdx = x mod 8
+    const int g = t / (kGroupRows * nt), r = t - g * (kGroupRows * nt);
+    const int gm = min(kGroupRows, mt - g * kGroupRows);      // rows in this (maybe ragged) group
+    tm = g * kGroupRows + r % gm;
+    tn = r / gm;
   }
   const int m0 = tm * kBM, n0 = tn * kBN;
   const int64_t kb = (int64_t)p.K * 2;             // row stride in bytes (X and W)
@@ -134,44 +125,69 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_gemm_kernel(FfnGemmParams 
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = f32x16{};
 
-  // ---- k loop: stage kt + kStages - 1 is copied while stage kt is multiplied
+  // ---- k loop over a two-stage ring. The barrier of stage kt sits before its last k step,
+  // whose operands are already in registers: past it no wave reads slot kt any more and
+  // stage kt + 1 is visible, so that step's products run while the operands of stage
+  // kt + 1's first step are read and stage kt + 2 is copied into slot kt. Within a step,
+  // one operand read of the next step and one copy go between consecutive products
+  // (a scheduling fence after each product keeps that order).
+  static_assert(kStages == 2 && MB == 4 && 2 * kCopiesPerWave == 16, "one copy per product");
   const int KT = p.K / kBK;
+  auto copy_one = [&](int s, int j) {   // copy j (X then W) of stage s into its slot
+    const unsigned slot = ring + (unsigned)(s & 1) * kStageBytes;
+    if (j < kCopiesPerWave)
+      dma::copy16(xbase + (int64_t)s * kRowBytes, cx.off[j], slot + (w + kWaves * j) * 1024);
+    else
+      dma::copy16(wbase + (int64_t)s * kRowBytes, cw.off[j - kCopiesPerWave],
+                  slot + kTileBytes + (w + kWaves * (j - kCopiesPerWave)) * 1024);
+  };
+  auto read_one = [&](unsigned st, unsigned off, int i, u32x4 (&an)[4], u32x4 (&bn)[MB]) {
+    if (i < 4) an[i] = *reinterpret_cast<const lds_u32x4*>(dma::lds_ptr(st + wrow + off) + i * 32 * kRowBytes);
+    else bn[i - 4] = *reinterpret_cast<const lds_u32x4*>(dma::lds_ptr(st + xrow + off) + (i - 4) * 32 * kRowBytes);
+  };
 #pragma unroll
-  for (int s = 0; s < kStages - 1; ++s) {
-    if (s < KT) {
-      cx.issue(xbase + (int64_t)s * kRowBytes, ring + s * kStageBytes, w);
-      cw.issue(wbase + (int64_t)s * kRowBytes, ring + s * kStageBytes + kTileBytes, w);
-    }
+  for (int j = 0; j < 16; ++j) copy_one(0, j);
+  if (KT > 1) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) copy_one(1, j);
+    dma::wait_vmcnt<16>();                            // stage 0 landed
+  } else {
+    dma::wait_vmcnt<0>();
   }
-  dma::wait_vmcnt<(kStages - 2) * 2 * kCopiesPerWave>();          // stage 0 landed
   __syncthreads();
+  u32x4 a[2][4], b[2][MB];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) read_one(ring, opoff[0], i, a[0], b[0]);
 
-  for (int kt = 0; kt < KT; ++kt) {
-    const unsigned st = ring + (unsigned)(kt % kStages) * kStageBytes;
-    const bool more = kt + kStages - 1 < KT;
-    if (more) {
-      const unsigned nx = ring + (unsigned)((kt + kStages - 1) % kStages) * kStageBytes;
-      cx.issue(xbase + (int64_t)(kt + kStages - 1) * kRowBytes, nx, w);
-      cw.issue(wbase + (int64_t)(kt + kStages - 1) * kRowBytes, nx + kTileBytes, w);
-    }
-    // k steps of 16: the operands of step ks + 1 are read while the products of step ks
-    // run (two register sets); a scheduling fence after each step keeps that order
-    u32x4 a[2][4], b[2][MB];
-    load_step(st + wrow, st + xrow, opoff[0], a[0], b[0]);
+  // stage kt; NEXT: a stage follows, COPY: stage kt + 2 exists (both known at compile time)
+  auto run_stage = [&](int kt, auto next_c, auto copy_c) {
+    constexpr bool NEXT = decltype(next_c)::value, COPY = decltype(copy_c)::value;
+    const unsigned st = ring + (unsigned)(kt & 1) * kStageBytes;
+    const unsigned st1 = ring + (unsigned)((kt + 1) & 1) * kStageBytes;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      if (ks + 1 < KS) load_step(st + wrow, st + xrow, opoff[ks + 1], a[(ks + 1) & 1], b[(ks + 1) & 1]);
+      const int cur = ks & 1, nxt = cur ^ 1;
+      if (NEXT && ks == KS - 1) {
+        dma::wait_vmcnt<0>();                         // stage kt + 1 landed
+        __syncthreads();
+      }
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = mfma_32x32x16(a[ks & 1][nb], b[ks & 1][mb], acc[nb][mb]);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < 16; ++i) {
+        if (i < 8) {
+          if (ks + 1 < KS) read_one(st, opoff[ks + 1], i, a[nxt], b[nxt]);
+          else if (NEXT) read_one(st1, opoff[0], i, a[nxt], b[nxt]);
+        }
+        if (COPY && ks == KS - 1) copy_one(kt + 2, i);
+        acc[i / MB][i % MB] = mfma_32x32x16(a[cur][i / MB], b[cur][i % MB], acc[i / MB][i % MB]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    // stage kt + 1 must have landed; the copies of the stages after it may still fly
-    if (more) dma::wait_vmcnt<(kStages - 2) * 2 * kCopiesPerWave>();
-    else dma::wait_vmcnt<0>();
-    __syncthreads();
-  }
+  };
+  int kt = 0;
+  for (; kt + 2 < KT; ++kt) run_stage(kt, std::true_type{}, std::true_type{});
+  if (kt + 1 < KT) run_stage(kt++, std::true_type{}, std::false_type{});
+  run_stage(kt, std::false_type{}, std::false_type{});
+  __syncthreads();   // every wave is done with the ring before the epilogue stages through it
 
 // ---- epilogue: bias, activation and bf16 rounding in registers, then the wave's
   // kWaveRows x 128 tile goes through LDS (the ring is free after the last barrier) so that

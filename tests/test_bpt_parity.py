@@ -60,6 +60,8 @@ SMALL = [
     # B, Hq, Hkv, S, d, block_rows
     (1, 2, 2, 100, 64, 64), (2, 2, 1, 130, 64, 32), (1, 4, 2, 257, 64, 100), (1, 2, 2, 200, 128, 200),
     (1, 1, 1, 1, 64, 16), (2, 2, 2, 96, 64, 1000),
+    # 11 x 2 tiles in the first product: a ragged group of the grouped tile order
+    (1, 2, 2, 2700, 64, 2700),
 ]
 
 
