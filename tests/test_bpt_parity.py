@@ -62,6 +62,8 @@ SMALL = [
     (1, 1, 1, 1, 64, 16), (2, 2, 2, 96, 64, 1000),
     # 11 x 2 tiles in the first product: a ragged group of the grouped tile order
     (1, 2, 2, 2700, 64, 2700),
+    # d_model 192 and 320: odd numbers of 64-wide k stages (3 and 5) in the first product
+    (1, 3, 3, 150, 64, 64), (2, 5, 5, 70, 64, 70),
 ]
 
 
