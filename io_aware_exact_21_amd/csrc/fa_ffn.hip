@@ -23,9 +23,10 @@
 // next k step are read, one 16-byte read between consecutive products, while the current
 // step's products run, and the stage's barrier sits before its last k step, whose operands
 // are already in registers. Past that barrier the last step's products overlap the reads
-// of the next stage's first operands and the copies of the stage after it. (With the
-// barrier at the stage end and the compiler's own placement of the reads, each step
-// waited for its operands and the matrix cores were busy 52% of the time.)
+// of the next stage's first operands and the first half of the copies of the stage after
+// it; the second half goes out during the next step. (With the barrier at the stage end
+// and the compiler's own placement of the reads, each step waited for its operands and the
+// matrix cores were busy 52% of the time; with all sixteen copies in one step, 64%.)
 #include <type_traits>
 
 #include "fa_bpt.hpp"
@@ -128,10 +129,13 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_gemm_kernel(FfnGemmParams 
   // ---- k loop over a two-stage ring. The barrier of stage kt sits before its last k step,
   // whose operands are already in registers: past it no wave reads slot kt any more and
   // stage kt + 1 is visible, so that step's products run while the operands of stage
-  // kt + 1's first step are read and stage kt + 2 is copied into slot kt. Within a step,
-  // one operand read of the next step and one copy go between consecutive products
-  // (a scheduling fence after each product keeps that order).
-  static_assert(kStages == 2 && MB == 4 && 2 * kCopiesPerWave == 16, "one copy per product");
+  // kt + 1's first step are read. The sixteen copies of stage kt + 2 into slot kt go out in
+  // two halves, one copy before every second product: the first half in that last step of
+  // stage kt, the second in the first step of stage kt + 1 (slot kt is then still unread,
+  // and both halves have landed by the wait before the barrier in stage kt + 1). Within a
+  // step, one operand read of the next step goes between consecutive products of its first
+  // half (a scheduling fence after each product keeps that order).
+  static_assert(kStages == 2 && MB == 4 && 2 * kCopiesPerWave == 16, "eight copies per half stage");
   const int KT = p.K / kBK;
   auto copy_one = [&](int s, int j) {   // copy j (X then W) of stage s into its slot
     const unsigned slot = ring + (unsigned)(s & 1) * kStageBytes;
@@ -149,8 +153,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_gemm_kernel(FfnGemmParams 
   for (int j = 0; j < 16; ++j) copy_one(0, j);
   if (KT > 1) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) copy_one(1, j);
-    dma::wait_vmcnt<16>();                            // stage 0 landed
+    for (int j = 0; j < 8; ++j) copy_one(1, j);     // the second half goes out in stage 0
+    dma::wait_vmcnt<8>();                             // stage 0 landed
   } else {
     dma::wait_vmcnt<0>();
   }
@@ -159,7 +163,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_gemm_kernel(FfnGemmParams 
 #pragma unroll
   for (int i = 0; i < 8; ++i) read_one(ring, opoff[0], i, a[0], b[0]);
 
-  // stage kt; NEXT: a stage follows, COPY: stage kt + 2 exists (both known at compile time)
+  // stage kt; NEXT: stage kt + 1 exists, COPY: stage kt + 2 exists (known at compile time)
   auto run_stage = [&](int kt, auto next_c, auto copy_c) {
     constexpr bool NEXT = decltype(next_c)::value, COPY = decltype(copy_c)::value;
     const unsigned st = ring + (unsigned)(kt & 1) * kStageBytes;
@@ -177,7 +181,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_gemm_kernel(FfnGemmParams 
           if (ks + 1 < KS) read_one(st, opoff[ks + 1], i, a[nxt], b[nxt]);
           else if (NEXT) read_one(st1, opoff[0], i, a[nxt], b[nxt]);
         }
-        if (COPY && ks == KS - 1) copy_one(kt + 2, i);
+        if ((i & 1) == 0) {
+          if (COPY && ks == KS - 1) copy_one(kt + 2, i >> 1);       // first half of stage kt + 2
+          if (NEXT && ks == 0) copy_one(kt + 1, 8 + (i >> 1));      // second half of stage kt + 1
+        }
         acc[i / MB][i % MB] = mfma_32x32x16(a[cur][i / MB], b[cur][i % MB], acc[i / MB][i % MB]);
         __builtin_amdgcn_sched_barrier(0);
       }
